@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Causal attention fwd+bwd throughput on one MI355X, with roofline and CPU-oracle baseline.
+
+A step is one fa_forward + fa_backward over the workload's seeded inputs, which are resident
+in HBM before the timed region starts. Counted work (the metric's convention): forward
+4*B*H*N^2*d FLOPs, halved when causal; backward 2.5x forward.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line. Extra modes for profiling runs:
+    --copy-calibration   run only a plain device copy of known size (HBM counter scaling)
+    --all                also print a per-workload table to stderr
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "b8_n4096_d64"
+KERNEL_SOURCES = ["tiled_attention_causal_amd/csrc/fa_bf16.hip",
+                  "tiled_attention_causal_amd/csrc/fa_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="stop the oracle sample after this much CPU work")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--all", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per backward launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"bwd_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_workload(w, steps, warmup):
+    import torch
+    from seeded_inputs import workload_inputs
+    from tiled_attention_causal_amd import fa_backward, fa_forward
+
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # Whole-step wall time over exactly `steps` steps.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    # Per-launch durations with events on the stream the kernels run on.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        ev[i][1].record(stream)
+        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize(dev)
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    return {
+        "ms_per_step": wall * 1e3 / steps,
+        "fwd_ms_mean": sum(fwd_ms) / steps,
+        "bwd_ms_mean": sum(bwd_ms) / steps,
+        "fwd_ms_median": fwd_ms[steps // 2],
+        "bwd_ms_median": bwd_ms[steps // 2],
+    }
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on whole heads of the same workload until `budget_s` is spent."""
+    import numpy as np
+
+    import oracle
+    from seeded_inputs import to_f64, workload_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = workload_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        a = [to_f64(inp[n][b, h]) for n in ("q", "k", "v", "do")]
+        oracle.head_forward(a[0], a[1], a[2], w.causal, w.scale)
+        oracle.head_backward(a[0], a[1], a[2], a[3], w.causal, w.scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = w.counted_flops()["total"] * done / len(heads)
+    del np
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (one head: B=1,H=1,N={w.Nq},d={w.d}), "
+                      f"fp64 forward + backward, {el:.1f} s; counted FLOPs as on the GPU"}
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path is "
+              "not sharded across GPUs.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    from seeded_inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (cuda:0 on ROCm)", file=sys.stderr)
+        sys.exit(1)
+    import tiled_attention_causal_amd
+    tiled_attention_causal_amd.load()  # fail loudly if the HIP library is missing
+
+    w = WORKLOADS[args.workload]
+    fl = w.counted_flops()
+    r = time_workload(w, args.steps, args.warmup)
+    value = fl["total"] / (r["ms_per_step"] * 1e-3) / 1e12
+    bwd_tf = fl["bwd"] / (r["bwd_ms_mean"] * 1e-3) / 1e12
+    fwd_tf = fl["fwd"] / (r["fwd_ms_mean"] * 1e-3) / 1e12
+
+    if args.all:
+        for name, ww in WORKLOADS.items():
+            rr = time_workload(ww, max(5, args.steps // 5), 3)
+            f2 = ww.counted_flops()
+            print(f"{name:18s} fwd {rr['fwd_ms_median']:.4f} ms "
+                  f"({f2['fwd'] / rr['fwd_ms_median'] / 1e9:.1f} TF/s)  bwd "
+                  f"{rr['bwd_ms_median']:.4f} ms ({f2['bwd'] / rr['bwd_ms_median'] / 1e9:.1f} TF/s)"
+                  f"  step {rr['ms_per_step']:.4f} ms "
+                  f"({f2['total'] / rr['ms_per_step'] / 1e9:.1f} TF/s)", file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": "causal attention fwd+bwd TFLOP/s (bf16, d=64) and % of MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "input_dtype": w.dtype},
+        "passes": {"fwd_ms": round(r["fwd_ms_mean"], 5), "fwd_tflops": round(fwd_tf, 2),
+                   "bwd_ms": round(r["bwd_ms_mean"], 5), "bwd_tflops": round(bwd_tf, 2)},
+        "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(bwd_tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

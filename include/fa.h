@@ -1,0 +1,138 @@
+/*
+ * fa.h -- C ABI of libfa.so: FlashAttention-2 style attention forward and backward on one
+ * MI355X (gfx950) GPU.
+ *
+ * Operation (defined in "Systems and Parallelism", CS336 field map, A2, section 1.2-1.3,
+ * problems flash_forward and flash_backward): for every (b, h),
+ *
+ *     S = Q K^T * scale,  causal: key j visible to query i iff j <= i (top-left),
+ *     P = row softmax of S over the visible keys,   O = P V,
+ *     L_i = logsumexp_j S_ij  (natural log; the only state the backward needs),
+ *
+ * and the analytic backward with upstream gradient dO,
+ *
+ *     dV = P^T dO,   dP = dO V^T,   D_i = sum_k dO_ik O_ik,   dS = P o (dP - D),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,
+ *
+ * where the backward rebuilds P = exp(S - L) from Q, K and L instead of storing it.
+ *
+ * Layout: every tensor is dense, row-major [B, H, N, d] (element (b,h,n,k) at
+ * ((b*H + h)*N + n)*d + k); L is dense [B, H, Nq] float32. Q, dO, O, dQ have N = Nq;
+ * K, V, dK, dV have N = Nk. Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype`;
+ * accumulation is float32 in every case. Data pointers must be 16-byte aligned.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller. The library allocates
+ * and frees nothing, keeps no state between calls and is re-entrant. Outputs must not alias
+ * inputs.
+ *
+ * Asynchrony: each call validates its arguments on the host, enqueues its kernels on
+ * `stream` (a hipStream_t; NULL means the default stream) and returns. Results are ready
+ * once the stream has been synchronised. A fault inside a kernel surfaces at that
+ * synchronisation, as for any HIP kernel.
+ *
+ * Errors: argument problems are reported synchronously, before anything is enqueued:
+ *   FA_ERROR_INVALID_VALUE  negative size, Nk == 0 while B*H*Nq > 0, a NULL or misaligned
+ *                           pointer that the call would touch, non-finite scale, or a
+ *                           workspace smaller than fa_backward_workspace_bytes();
+ *   FA_ERROR_NOT_SUPPORTED  unknown dtype, d not in {16, 32, 64, 128}, or a size above the
+ *                           limits below;
+ *   FA_ERROR_LAUNCH_FAILED  the HIP runtime rejected a kernel launch.
+ * No C++ exception crosses this interface.
+ *
+ * Limits: Nq, Nk <= 2^24, B*H <= 2^31 - 1 and B*H*(ceil(Nq/32) + ceil(Nk/32)) < 2^24
+ * (launch grids count work-items in 32 bits). Any positive Nq, Nk is accepted (ragged
+ * tiles are masked); Nq != Nk is allowed. B*H*Nq == 0 makes fa_forward a no-op; in
+ * fa_backward, Nq == 0 with Nk > 0 writes dK = dV = 0.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FA_API __attribute__((visibility("default")))
+#else
+#define FA_API
+#endif
+
+typedef enum fa_status {
+  FA_SUCCESS = 0,
+  FA_ERROR_INVALID_VALUE = 1,
+  FA_ERROR_NOT_SUPPORTED = 2,
+  FA_ERROR_LAUNCH_FAILED = 3
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_DTYPE_F32 = 0,  /* IEEE binary32 in and out                           */
+  FA_DTYPE_BF16 = 1  /* bfloat16 in and out; outputs rounded to nearest even */
+} fa_dtype;
+
+/*
+ * fa_forward -- O = softmax(Q K^T * scale [+ causal mask]) V and L = row logsumexp.
+ *
+ * Follows problem flash_forward: the kernel walks key tiles with an online softmax
+ * (running row max m and row sum l, rescaling the accumulator when m grows), divides by l
+ * once at the end and writes L = scale*m + log(l); with is_causal it skips key tiles above
+ * the diagonal and masks only the diagonal tiles.
+ *
+ *   dtype        FA_DTYPE_F32 or FA_DTYPE_BF16
+ *   B, H         batch and head counts (>= 0)
+ *   Nq, Nk       query and key counts (>= 0)
+ *   d            head dimension: 16, 32, 64 or 128
+ *   Q            [B,H,Nq,d] dtype, read
+ *   K, V         [B,H,Nk,d] dtype, read
+ *   is_causal    0: all keys visible; nonzero: key j visible to query i iff j <= i
+ *   scale        multiplies Q K^T (finite; usually 1/sqrt(d))
+ *   O            [B,H,Nq,d] dtype, written
+ *   L            [B,H,Nq] float32, written (natural-log logsumexp of the scaled scores)
+ *   stream       hipStream_t or NULL
+ */
+FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     const void* Q, const void* K, const void* V, int is_causal, float scale,
+                     void* O, float* L, void* stream);
+
+/*
+ * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs for these
+ * sizes. The current kernels compute D = rowsum(dO o O) inside the backward kernel and
+ * need none, so this returns 0; callers should still ask, and pass at least this much.
+ */
+FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                   int64_t Nk, int64_t d);
+
+/*
+ * fa_backward -- dQ, dK, dV of O = softmax(Q K^T * scale [+ causal mask]) V.
+ *
+ * Follows problem flash_backward and the two-pass split of section 1.3.3: P is rebuilt as
+ * exp(S - L) from Q, K and the forward's L; D_i = sum_k dO_ik O_ik; one set of workgroups
+ * walks query tiles for each key tile and accumulates dK and dV, another walks key tiles
+ * for each query tile and accumulates dQ, so no output is ever updated atomically and the
+ * result is bitwise deterministic. The scale appears once in dQ and once in dK.
+ *
+ *   Q, K, V, is_causal, scale   exactly as given to fa_forward
+ *   O, L                        fa_forward's outputs for those inputs
+ *   dO                          [B,H,Nq,d] dtype, upstream gradient
+ *   dQ                          [B,H,Nq,d] dtype, written
+ *   dK, dV                      [B,H,Nk,d] dtype, written
+ *   workspace, workspace_bytes  device scratch of at least fa_backward_workspace_bytes()
+ *                               bytes (may be NULL when that is 0)
+ *   stream                      hipStream_t or NULL
+ */
+FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const float* L, const void* dO, int is_causal, float scale,
+                      void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* fa_status_string -- static, NUL-terminated name of a status code (never NULL). */
+FA_API const char* fa_status_string(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,134 @@
+"""libfa.so loads, exports every symbol include/fa.h declares, and validates arguments.
+
+These run without a GPU: every call below returns from host-side validation before the
+library touches the HIP runtime (no kernel is launched, no pointer is dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tiled_attention_causal_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfa.so is not built; run `python -m tiled_attention_causal_amd.build`")
+    return _lib.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_symbols() == ["fa_backward", "fa_backward_workspace_bytes", "fa_forward",
+                                  "fa_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from tiled_attention_causal_amd import _lib
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_only_the_c_abi_is_exported():
+    from tiled_attention_causal_amd import _lib
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    text_syms = sorted(ln.split()[-1] for ln in out.splitlines() if " T " in ln)
+    assert text_syms == declared_symbols()
+
+
+def test_status_strings(lib):
+    names = {0: "FA_SUCCESS", 1: "FA_ERROR_INVALID_VALUE", 2: "FA_ERROR_NOT_SUPPORTED",
+             3: "FA_ERROR_LAUNCH_FAILED"}
+    for code, name in names.items():
+        assert lib.fa_status_string(code).decode() == name
+    assert lib.fa_status_string(77).decode() == "FA_UNKNOWN_STATUS"
+
+
+def test_workspace_is_zero(lib):
+    for dt in (0, 1):
+        assert lib.fa_backward_workspace_bytes(dt, 8, 1, 4096, 4096, 64) == 0
+
+
+# A fake, 16-byte aligned address. Only passed where validation must fail first (or where
+# the call is a no-op), so it is never dereferenced.
+P = 0x10000
+BAD = 0x10002  # misaligned
+
+
+def fwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, causal=1, scale=0.125,
+        o=P, lse=P):
+    return lib.fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o, lse, None)
+
+
+def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
+        causal=1, scale=0.125, dq=P, dk=P, dv=P, ws=None, ws_bytes=0):
+    return lib.fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, lse, do, causal, scale, dq, dk,
+                           dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(d=48), 2), (dict(d=256), 2), (dict(d=0), 1), (dict(d=-64), 1),
+    (dict(B=-1), 1), (dict(H=-1), 1), (dict(Nq=-1), 1), (dict(Nk=-5), 1),
+    (dict(Nk=0), 1),
+    (dict(Nq=(1 << 24) + 1), 2), (dict(B=1 << 20, H=1 << 12), 2),
+    (dict(scale=math.inf), 1), (dict(scale=math.nan), 1),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(lse=None), 1), (dict(q=BAD), 1), (dict(o=BAD), 1),
+])
+def test_forward_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0), dict(Nq=0, Nk=0, q=None,
+                                                                        k=None, v=None, o=None,
+                                                                        lse=None)])
+def test_forward_empty_is_a_noop(lib, kw):
+    assert fwd(lib, **kw) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 2), (dict(d=24), 2), (dict(Nq=-1), 1), (dict(Nk=0), 1),
+    (dict(scale=-math.inf), 1),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(dk=BAD), 1),
+    (dict(Nq=0, dk=None), 1),  # Nq == 0 still writes dK and dV
+])
+def test_backward_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_backward_empty_is_a_noop(lib):
+    assert bwd(lib, B=0) == 0
+    assert bwd(lib, Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None,
+               dk=None, dv=None) == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from tiled_attention_causal_amd import fa_forward
+    x = torch.zeros(1, 1, 16, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa_forward(x, x, x, True)
+
+
+def test_signature_table_matches_header_argument_counts():
+    from tiled_attention_causal_amd import _lib
+    text = open(HEADER).read()
+    for name in declared_symbols():
+        m = re.search(r"FA_API[\w\s\*]+?\b" + name + r"\s*\(([^)]*)\)", text)
+        nargs = len([a for a in m.group(1).split(",") if a.strip()])
+        assert nargs == len(_lib.SIGNATURES[name][1]), name

@@ -1,0 +1,9 @@
+"""FlashAttention-2 style causal attention for MI355X (gfx950): HIP kernels behind a C ABI.
+
+    from tiled_attention_causal_amd import fa_forward, fa_backward, FlashAttention
+"""
+from ._lib import FAError, LIB_PATH, load  # noqa: F401
+from .ops import FlashAttention, default_scale, fa_backward, fa_forward  # noqa: F401
+
+__all__ = ["fa_forward", "fa_backward", "FlashAttention", "default_scale", "FAError", "load",
+           "LIB_PATH"]

@@ -1,0 +1,119 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation and kernel dispatch.
+// Nothing here allocates, and no error leaves as a C++ exception.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxBH = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxGroups = (int64_t(1) << 24) - 1;
+
+bool supported_d(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by both entry points; on success fills *s. Pointer checks come later,
+// once the caller knows which tensors a call will touch.
+fa_status check_common(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                       float scale, int is_causal, fa::Shape* s) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERROR_INVALID_VALUE;
+  if (!supported_d(d)) return FA_ERROR_NOT_SUPPORTED;
+  if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
+  if (Nq > kMaxN || Nk > kMaxN) return FA_ERROR_NOT_SUPPORTED;
+  if (H != 0 && B > kMaxBH / H) return FA_ERROR_NOT_SUPPORTED;
+  const int64_t BH = B * H;
+  // Launch grids count work-items in 32 bits: with 256-thread workgroups every grid here
+  // stays below BH * (ceil(Nq/32) + ceil(Nk/32)) < 2^24 workgroups.
+  if (BH > 0 && ((Nq + 31) / 32 + (Nk + 31) / 32) > (kMaxGroups / BH))
+    return FA_ERROR_NOT_SUPPORTED;
+  s->BH = static_cast<int>(BH);
+  s->Nq = static_cast<int>(Nq);
+  s->Nk = static_cast<int>(Nk);
+  s->d = static_cast<int>(d);
+  s->causal = is_causal != 0;
+  s->scale = scale;
+  return FA_SUCCESS;
+}
+
+bool bad_ptr(const void* p) { return p == nullptr || !aligned16(p); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_SUCCESS:
+      return "FA_SUCCESS";
+    case FA_ERROR_INVALID_VALUE:
+      return "FA_ERROR_INVALID_VALUE";
+    case FA_ERROR_NOT_SUPPORTED:
+      return "FA_ERROR_NOT_SUPPORTED";
+    case FA_ERROR_LAUNCH_FAILED:
+      return "FA_ERROR_LAUNCH_FAILED";
+  }
+  return "FA_UNKNOWN_STATUS";
+}
+
+size_t fa_backward_workspace_bytes(fa_dtype, int64_t, int64_t, int64_t, int64_t, int64_t) {
+  return 0;
+}
+
+fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     const void* Q, const void* K, const void* V, int is_causal, float scale,
+                     void* O, float* L, void* stream) {
+  fa::Shape s;
+  const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
+  if (st != FA_SUCCESS) return st;
+  if ((int64_t)s.BH * Nq == 0) return FA_SUCCESS;
+  if (Nk == 0) return FA_ERROR_INVALID_VALUE;  // softmax over no keys
+  if (bad_ptr(Q) || bad_ptr(K) || bad_ptr(V) || bad_ptr(O) || L == nullptr ||
+      (reinterpret_cast<uintptr_t>(L) & 3u) != 0)
+    return FA_ERROR_INVALID_VALUE;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_DTYPE_BF16)
+    e = fa::launch_fwd_bf16(s, Q, K, V, O, L, hs);
+  else
+    e = fa::launch_fwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
+                           static_cast<const float*>(V), static_cast<float*>(O), L, hs);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
+fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const float* L, const void* dO, int is_causal, float scale, void* dQ,
+                      void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  fa::Shape s;
+  const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
+  if (st != FA_SUCCESS) return st;
+  if (workspace_bytes < fa_backward_workspace_bytes(dtype, B, H, Nq, Nk, d))
+    return FA_ERROR_INVALID_VALUE;
+  (void)workspace;
+  const bool has_q = (int64_t)s.BH * Nq > 0, has_k = (int64_t)s.BH * Nk > 0;
+  if (!has_q && !has_k) return FA_SUCCESS;
+  if (has_q && Nk == 0) return FA_ERROR_INVALID_VALUE;  // softmax over no keys
+  if (has_q && (bad_ptr(Q) || bad_ptr(O) || bad_ptr(dO) || bad_ptr(dQ) || L == nullptr ||
+                (reinterpret_cast<uintptr_t>(L) & 3u) != 0))
+    return FA_ERROR_INVALID_VALUE;
+  if (has_k && (bad_ptr(K) || bad_ptr(V) || bad_ptr(dK) || bad_ptr(dV)))
+    return FA_ERROR_INVALID_VALUE;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_DTYPE_BF16)
+    e = fa::launch_bwd_bf16(s, Q, K, V, O, L, dO, dQ, dK, dV, hs);
+  else
+    e = fa::launch_bwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
+                           static_cast<const float*>(V), static_cast<const float*>(O), L,
+                           static_cast<const float*>(dO), static_cast<float*>(dQ),
+                           static_cast<float*>(dK), static_cast<float*>(dV), hs);
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
+}  // extern "C"

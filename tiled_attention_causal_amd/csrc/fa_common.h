@@ -1,0 +1,115 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, the bf16 MFMA,
+// swizzled LDS tile addressing, cross-lane reductions and the workgroup-to-XCD remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
+// Fragment layout with g = lane / 32:
+//   A: lane holds row (lane % 32), k = 8g .. 8g+7;  B: lane holds column (lane % 32), same k;
+//   C: register r holds row 8*(r/4) + 4g + (r%4), column (lane % 32).
+// The k order inside a fragment only has to agree between A and B, which it does for any
+// tile this file reads with the same chunk index.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Eight consecutive fp32 accumulator registers -> one bf16 MFMA operand (RNE).
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& x, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)x[base + e];
+  return r;
+}
+
+// Position of row index m (0..31 inside a 32-row block pair of 16-steps) in a transposed
+// tile. An MFMA C fragment leaves, in lane group g, rows 16t + 8a + 4g + b (a in {0,1},
+// b in 0..3) of step t; storing row 16t + 8a + 4g + b at column 16t + 8g + 4a + b makes the
+// eight values a lane group needs for step t one contiguous 16-byte chunk: chunk 2t + g.
+__device__ __forceinline__ int tpos(int m) {
+  return (m & ~15) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+// Row m of the e-th element (e = 0..7) of transposed chunk kc: inverse of tpos.
+__device__ __forceinline__ int chunk_row(int kc, int e) {
+  return 16 * (kc >> 1) + 8 * (e >> 2) + 4 * (kc & 1) + (e & 3);
+}
+
+// Element offset of 16-byte chunk c of row r in an LDS tile with NCH chunks per row and no
+// padding. Chunks are XOR-swizzled by (r ^ r>>3) so that eight consecutive rows reading the
+// same chunk, and rows 8 apart writing the same chunk, fall in different bank groups.
+template <int NCH>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int M = NCH < 8 ? NCH - 1 : 7;
+  return r * (NCH * 8) + ((c ^ ((r ^ (r >> 3)) & M)) << 3);
+}
+
+template <int NCH>
+__device__ __forceinline__ bf16x8 lds_frag(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + swz<NCH>(r, c));
+}
+
+// All-reduce (sum) across aligned groups of N lanes (N = 1, 2, 4, 8, 16 or 32).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8)  // row_half_mirror: lane i <- lane 7-i inside each 8
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16)  // row_mirror: lane i <- lane 15-i inside each 16
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                            0x140, 0xF, 0xF, false));
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Value held by lane (lane ^ 32).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// Workgroups are dispatched round-robin over the eight XCDs (workgroup b runs on XCD b % 8).
+// Give each XCD one contiguous range of logical tiles so that the tiles of a head, which
+// re-read the same K/V (or Q/dO) rows, share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  if ((n & 7) != 0) return bid;
+  return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+// Pack element `sel` (0 or 1) of two bf16 pairs into one pair: (a.sel, b.sel).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+"""Python entry points over libfa.so: fa_forward, fa_backward and an autograd.Function.
+
+PyTorch supplies device memory and the current stream; the library does all the work.
+Shapes follow "Systems and Parallelism" (CS336 field map, A2), problem flash_forward:
+forward(Q, K, V, is_causal=False) returns O, and the only [batch, n_queries]-shaped tensor
+saved for the backward is the logsumexp L.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.FA_DTYPE_F32, torch.bfloat16: _lib.FA_DTYPE_BF16}
+
+
+def default_scale(d: int) -> float:
+    """float32(1/sqrt(d)), the value passed to the kernels when no scale is given."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def _stream_ptr(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(name: str, t: torch.Tensor, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device} (a GPU device), got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _raise(status: int, where: str):
+    if status != _lib.FA_SUCCESS:
+        raise _lib.FAError(status, where)
+
+
+def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
+               scale: float | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None):
+    """O, L = attention forward on [B, H, N, d] tensors (bf16 or fp32)."""
+    lib = _lib.load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2] if k.dim() == 4 else -1
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _check("q", q, (B, H, Nq, d), q.dtype, q.device)
+    _check("k", k, (B, H, Nk, d), q.dtype, q.device)
+    _check("v", v, (B, H, Nk, d), q.dtype, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check("out", out, (B, H, Nq, d), q.dtype, q.device)
+    _check("lse", lse, (B, H, Nq), torch.float32, q.device)
+    sc = default_scale(d) if scale is None else float(scale)
+    st = lib.fa_forward(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
+                        v.data_ptr(), int(bool(is_causal)), sc, out.data_ptr(), lse.data_ptr(),
+                        _stream_ptr(q))
+    _raise(st, "fa_forward")
+    return out, lse
+
+
+def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                lse: torch.Tensor, do: torch.Tensor, is_causal: bool = False,
+                scale: float | None = None, dq: torch.Tensor | None = None,
+                dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """dQ, dK, dV of the attention forward, from Q, K, V, O, L and dO."""
+    lib = _lib.load()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for name, t, n in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq), ("do", do, Nq)):
+        _check(name, t, (B, H, n, d), dt, q.device)
+    _check("lse", lse, (B, H, Nq), torch.float32, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, n in (("dq", dq, Nq), ("dk", dk, Nk), ("dv", dv, Nk)):
+        _check(name, t, (B, H, n, d), dt, q.device)
+    ws_bytes = lib.fa_backward_workspace_bytes(_DTYPES[dt], B, H, Nq, Nk, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    sc = default_scale(d) if scale is None else float(scale)
+    st = lib.fa_backward(_DTYPES[dt], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         o.data_ptr(), lse.data_ptr(), do.data_ptr(), int(bool(is_causal)), sc,
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q))
+    _raise(st, "fa_backward")
+    return dq, dk, dv
+
+
+class FlashAttention(torch.autograd.Function):
+    """Autograd wrapper: apply(Q, K, V, is_causal=False, scale=None) -> O."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, is_causal=False, scale=None):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = fa_forward(q, k, v, is_causal, scale)
+        ctx.save_for_backward(lse, q, k, v, o)
+        ctx.is_causal = bool(is_causal)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        lse, q, k, v, o = ctx.saved_tensors
+        dq, dk, dv = fa_backward(q, k, v, o, lse, do.contiguous(), ctx.is_causal, ctx.scale)
+        return dq, dk, dv, None, None
