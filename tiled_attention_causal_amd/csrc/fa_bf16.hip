@@ -46,16 +46,11 @@ struct TUnit {
   static constexpr int N = (MT / 8) * (D / 4);
   u32x2 r[8];
 
-  __device__ __forceinline__ void load(const bf16* head, int row0, int nrows, int u) {
+  __device__ __forceinline__ void load(rsrc_t head, int row0, int u) {
     const int d4 = u % (D / 4), kc = u / (D / 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = row0 + chunk_row(kc, e);
-      if (row < nrows)
-        r[e] = *reinterpret_cast<const u32x2*>(head + (size_t)row * D + 4 * d4);
-      else
-        r[e] = u32x2{0u, 0u};
-    }
+    for (int e = 0; e < 8; ++e)
+      r[e] = buf_load8(head, ((row0 + chunk_row(kc, e)) * D + 4 * d4) * 2);
   }
   // Row-major copy: tile[MT][D].
   __device__ __forceinline__ void store_rows(bf16* tile, int u) const {
@@ -89,15 +84,12 @@ struct RChunks {
   static constexpr int PER = (NC + NT - 1) / NT;
   u32x4 r[PER];
 
-  __device__ __forceinline__ void load(const bf16* head, int row0, int nrows, int t) {
+  __device__ __forceinline__ void load(rsrc_t head, int row0, int t) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int c = t + p * NT;
-      const int row = c / (D / 8), ch = c % (D / 8);
-      if (c < NC && row0 + row < nrows)
-        r[p] = *reinterpret_cast<const u32x4*>(head + (size_t)(row0 + row) * D + 8 * ch);
-      else
-        r[p] = u32x4{0u, 0u, 0u, 0u};
+      if (NC % NT == 0 || c < NC)
+        r[p] = buf_load16(head, ((row0 + c / (D / 8)) * D + 8 * (c % (D / 8))) * 2);
     }
   }
   __device__ __forceinline__ void store(bf16* tile, int t) const {
@@ -111,12 +103,10 @@ struct RChunks {
 
 // Stationary-row fragments: lane holds row `row`, d = 16s + 8g .. +7 for every step s.
 template <int D>
-__device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], const bf16* head, int row,
-                                           int nrows, int g) {
+__device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], rsrc_t head, int row, int g) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
-    f[s] = row < nrows ? *reinterpret_cast<const bf16x8*>(head + (size_t)row * D + 16 * s + 8 * g)
-                       : zero_bf16x8();
+    f[s] = __builtin_bit_cast(bf16x8, buf_load16(head, (row * D + 16 * s + 8 * g) * 2));
 }
 
 // Store a transposed 32-wide output block: lane owns row `row`; register r of block db holds
@@ -138,6 +128,54 @@ __device__ __forceinline__ void store_rows_from_acc(bf16* out_row, const f32x16 
     }
 }
 
+// Online-softmax update of one 32-query x 64-key score tile held as in fwd_kernel: lane =
+// query, register r of block kb = key offset 32kb + 8(r/4) + 4g + r%4 from the tile start.
+// Rows rescale only when their max grows by more than 2^8 (in exp2 units): until then the
+// stale max keeps every p <= 2^8, and O = acc / l does not depend on which max was used.
+template <bool MASKED, int DB>
+__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float& l,
+                                             f32x16 (&o)[DB], float c, bool first, int qlim,
+                                             int klim) {
+  constexpr float kLazy = 8.f;
+  auto vis = [&](int kb, int r) {
+    const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+    return off <= qlim && off < klim;
+  };
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      mx = fmaxf(mx, (!MASKED || vis(kb, r)) ? sacc[kb][r] : -INFINITY);
+  mx = fmaxf(mx, swap_halves(mx));
+  if (first) {
+    m = mx;  // every row sees key 0 in the first tile, so this is finite
+  } else {
+    const bool grow = (mx - m) * c > kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? fast_exp2((m - mx) * c) : 1.f;
+      m = grow ? mx : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+  }
+  const float nb = -m * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(sacc[kb][r], c, nb));
+      if (MASKED && !vis(kb, r)) p = 0.f;
+      sacc[kb][r] = p;
+      rs += p;
+    }
+  l += rs;
+}
+
 // ------------------------------------------------------------------------------ forward
 
 template <int D, bool CAUSAL>
@@ -157,9 +195,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   const int bh = lid / nqt;
   const int qt = CAUSAL ? nqt - 1 - lid % nqt : lid % nqt;  // longest rows first
   const int q0 = qt * BQ;
-  const bf16* Qh = Q + (size_t)bh * Nq * D;
-  const bf16* Kh = K + (size_t)bh * Nk * D;
-  const bf16* Vh = V + (size_t)bh * Nk * D;
+  const rsrc_t Qr = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 2);
+  const rsrc_t Kr = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
+  const rsrc_t Vr = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int qw0 = q0 + 32 * w;
@@ -171,7 +209,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   if (CAUSAL) nkt = min(nkt, (min(q0 + BQ, Nq) - 1) / BK + 1);
 
   bf16x8 qf[DS];
-  load_frags<D>(qf, Qh, qrow, Nq, g);
+  load_frags<D>(qf, Qr, qrow, g);
+  wait_vmem();  // keeps the loop's own prefetch waits exact
   if (neg)
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
@@ -179,12 +218,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
-  float m = -INFINITY, l = 0.f;
+  float m = 0.f, l = 0.f;
 
   RChunks<BK, D, 256> kreg;
   TUnit<BK, D> vreg;
-  kreg.load(Kh, 0, Nk, tid);
-  if (tid < NVU) vreg.load(Vh, 0, Nk, tid);
+  kreg.load(Kr, 0, tid);
+  if (tid < NVU) vreg.load(Vr, 0, tid);
   kreg.store(smem, tid);
   if (tid < NVU) vreg.store_trans(smem + KT, tid);
   __syncthreads();
@@ -193,63 +232,48 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
     const int buf = kt & 1;
     const bool more = kt + 1 < nkt;
     if (more) {
-      kreg.load(Kh, (kt + 1) * BK, Nk, tid);
-      if (tid < NVU) vreg.load(Vh, (kt + 1) * BK, Nk, tid);
+      kreg.load(Kr, (kt + 1) * BK, tid);
+      if (tid < NVU) vreg.load(Vr, (kt + 1) * BK, tid);
     }
     const int k0 = kt * BK;
     const bool active = qw0 < Nq && (!CAUSAL || k0 <= qw0 + 31);
     if (active) {
       const bf16* sK = smem + buf * BUF;
       const bf16* sV = sK + KT;
+      // All K fragments of the tile first, so the LDS latency is paid once.
+      bf16x8 kfr[2][DS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < DS; ++s) kfr[kb][s] = lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = zero16();
 #pragma unroll
-        for (int s = 0; s < DS; ++s)
-          sacc[kb] = mfma32(lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g), qf[s], sacc[kb]);
+        for (int s = 0; s < DS; ++s) sacc[kb] = mfma32(kfr[kb][s], qf[s], sacc[kb]);
       }
-      // Score registers: key k0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query.
-      // Only tiles that straddle the diagonal or the ragged end of K compare indices; the
-      // masked entries are left out of the row max and zeroed after the exponential, which
-      // stays exact for any finite scale (including 0).
-      const bool masked = (CAUSAL && k0 + BK - 1 > qw0) || k0 + BK > Nk;
-      auto vis = [&](int kb, int r) {
-        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        return key < Nk && (!CAUSAL || key <= qrow);
-      };
-      float mx = -INFINITY;
+      bf16x8 vfr[4][DB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mx = fmaxf(mx, (!masked || vis(kb, r)) ? sacc[kb][r] : -INFINITY);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m, mx);  // finite: every row sees key 0 in the first tile
-      const float alpha = m == -INFINITY ? 0.f : fast_exp2((m - mnew) * c);
-      const float nb = -mnew * c;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[kb][r], c, nb));
-          if (masked && !vis(kb, r)) p = 0.f;
-          sacc[kb][r] = p;
-          rs += p;
-        }
-      l = l * alpha + rs;
-      m = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        for (int db = 0; db < DB; ++db) vfr[u][db] = lds_frag<BK / 8>(sV, 32 * db + l32, 2 * u + g);
+      // Score registers: key k0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query. Only
+      // tiles that straddle the diagonal or the ragged end of K compare indices; masked
+      // entries are left out of the row max and zeroed after the exponential, which stays
+      // exact for any finite scale (including 0).
+      if ((CAUSAL && k0 + BK - 1 > qw0) || k0 + BK > Nk) {
+        const int qlim = CAUSAL ? qrow - k0 - 4 * g : 1 << 30;  // visible iff offset <= qlim
+        const int klim = Nk - k0 - 4 * g;                       // and offset < klim
+        softmax_tile<true>(sacc, m, l, o, c, kt == 0, qlim, klim);
+      } else {
+        softmax_tile<false>(sacc, m, l, o, c, kt == 0, 0, 0);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = mfma32(lds_frag<BK / 8>(sV, 32 * db + l32, 2 * u + g), pf, o[db]);
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf, o[db]);
       }
     }
     if (more) {
@@ -269,6 +293,46 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 
 // ----------------------------------------------------------------------------- backward
 
+// dK/dV pass: P = exp2(S c - L log2e) and dS = P (dP - D) in place, for score registers laid
+// out with lane = key and register r of block qb = query offset 32qb + 8(r/4) + 4g + r%4.
+// Masked (query < key) entries get P = dS = 0.
+template <bool MASKED, int NB>
+__device__ __forceinline__ void dkdv_scores(f32x16 (&sp)[NB], f32x16 (&dp)[NB],
+                                            const float* sL2, const float* sD, float c, int g,
+                                            int lim) {
+#pragma unroll
+  for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 32 * qb + 8 * j + 4 * g);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * qb + 8 * j + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        float p = fast_exp2(fmaf(sp[qb][r], c, -l4[i]));
+        if (MASKED && 32 * qb + 8 * j + i < lim) p = 0.f;
+        sp[qb][r] = p;
+        dp[qb][r] = p * (dp[qb][r] - d4[i]);
+      }
+    }
+}
+
+// dQ pass: the same for lane = query and register r of block kb = key offset
+// 32kb + 8(r/4) + 4g + r%4; visible iff offset <= qlim and offset < klim.
+template <bool MASKED, int NB>
+__device__ __forceinline__ void dq_scores(f32x16 (&st)[NB], f32x16 (&dpt)[NB], float c, float l2,
+                                          float dsum, int qlim, int klim) {
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(fmaf(st[kb][r], c, -l2));
+      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+      if (MASKED && (off > qlim || off >= klim)) p = 0.f;
+      dpt[kb][r] = p * (dpt[kb][r] - dsum);
+    }
+}
+
 template <int D>
 struct BwdCfg {
   static constexpr int MT = D >= 128 ? 32 : 64;  // moving-tile rows
@@ -286,10 +350,9 @@ struct BwdCfg {
 
 // dK, dV for the 128 keys starting at k0 of one head.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_part(bf16* smem, const bf16* Qh, const bf16* Kh,
-                                          const bf16* Vh, const bf16* Oh, const float* Lh,
-                                          const bf16* dOh, bf16* dKh, bf16* dVh, int k0, int Nq,
-                                          int Nk, float scale, int neg) {
+__device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
+                                          rsrc_t Lr, rsrc_t dOr, bf16* dKh, bf16* dVh, int k0,
+                                          int Nq, int Nk, float scale, int neg) {
   using C = BwdCfg<D>;
   constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -298,8 +361,9 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, const bf16* Qh, const bf16
   const float c = fabsf(scale) * kLog2e;
 
   bf16x8 kf[DS], vf[DS];
-  load_frags<D>(kf, Kh, krow, Nk, g);
-  load_frags<D>(vf, Vh, krow, Nk, g);
+  load_frags<D>(kf, Kr, krow, g);
+  load_frags<D>(vf, Vr, krow, g);
+  wait_vmem();
   if (neg)
 #pragma unroll
     for (int s = 0; s < DS; ++s) kf[s] = negate(kf[s]);
@@ -324,12 +388,12 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, const bf16* Qh, const bf16
 
   auto fetch = [&](int mt) {
     const int m0 = mt * MT;
-    if (q_role) qreg.load(Qh, m0, Nq, u);
+    if (q_role) qreg.load(Qr, m0, u);
     if (do_role) {
-      doreg.load(dOh, m0, Nq, u);
-      oreg.load(Oh, m0, Nq, u);
+      doreg.load(dOr, m0, u);
+      oreg.load(Or, m0, u);
     }
-    if (tid < MT) lreg = m0 + tid < Nq ? Lh[m0 + tid] : 0.f;
+    if (tid < MT) lreg = buf_load_f32(Lr, (m0 + tid) * 4);
   };
   auto stage = [&](int mt, bf16* base) {
     const int m0 = mt * MT;
@@ -383,39 +447,40 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, const bf16* Qh, const bf16
       f32x16 sp[NB], dp[NB];
 #pragma unroll
       for (int qb = 0; qb < NB; ++qb) {
+        bf16x8 qa[DS], da[DS];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          qa[s] = lds_frag<D / 8>(sQ, 32 * qb + l32, 2 * s + g);
+          da[s] = lds_frag<D / 8>(sdO, 32 * qb + l32, 2 * s + g);
+        }
         sp[qb] = zero16();
         dp[qb] = zero16();
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          sp[qb] = mfma32(lds_frag<D / 8>(sQ, 32 * qb + l32, 2 * s + g), kf[s], sp[qb]);
-          dp[qb] = mfma32(lds_frag<D / 8>(sdO, 32 * qb + l32, 2 * s + g), vf[s], dp[qb]);
+          sp[qb] = mfma32(qa[s], kf[s], sp[qb]);
+          dp[qb] = mfma32(da[s], vf[s], dp[qb]);
         }
       }
-      // Registers: query m0 + 32qb + 8(r/4) + 4g + r%4 against this lane's key.
-      const bool need_mask = CAUSAL && m0 < kw0 + 31;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 32 * qb + 8 * j + 4 * g);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * qb + 8 * j + 4 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i;
-            float p = fast_exp2(fmaf(sp[qb][r], c, -l4[i]));
-            if (need_mask && m0 + 32 * qb + 8 * j + 4 * g + i < krow) p = 0.f;
-            sp[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[i]);
-          }
-        }
+      // Registers: query m0 + 32qb + 8(r/4) + 4g + r%4 against this lane's key; the key is
+      // visible iff query >= key, i.e. offset 32qb + 8(r/4) + r%4 >= krow - m0 - 4g.
+      if (CAUSAL && m0 < kw0 + 31)
+        dkdv_scores<true, NB>(sp, dp, sL2, sD, c, g, krow - m0 - 4 * g);
+      else
+        dkdv_scores<false, NB>(sp, dp, sL2, sD, c, g, 0);
 #pragma unroll
       for (int st = 0; st < 2 * NB; ++st) {
+        bf16x8 ofr[DB], qfr[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          ofr[db] = lds_frag<MT / 8>(sdOt, 32 * db + l32, 2 * st + g);
+          qfr[db] = lds_frag<MT / 8>(sQt, 32 * db + l32, 2 * st + g);
+        }
         const bf16x8 pf = to_bf16x8(sp[st >> 1], 8 * (st & 1));
         const bf16x8 sf = to_bf16x8(dp[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvt[db] = mfma32(lds_frag<MT / 8>(sdOt, 32 * db + l32, 2 * st + g), pf, dvt[db]);
-          dkt[db] = mfma32(lds_frag<MT / 8>(sQt, 32 * db + l32, 2 * st + g), sf, dkt[db]);
+          dvt[db] = mfma32(ofr[db], pf, dvt[db]);
+          dkt[db] = mfma32(qfr[db], sf, dkt[db]);
         }
       }
     }
@@ -431,9 +496,9 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, const bf16* Qh, const bf16
 
 // dQ for the 128 queries starting at q0 of one head.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dq_part(bf16* smem, const bf16* Qh, const bf16* Kh, const bf16* Vh,
-                                        const bf16* Oh, const float* Lh, const bf16* dOh,
-                                        bf16* dQh, int q0, int Nq, int Nk, float scale, int neg) {
+__device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
+                                        rsrc_t Lr, rsrc_t dOr, bf16* dQh, int q0, int Nq, int Nk,
+                                        float scale, int neg) {
   using C = BwdCfg<D>;
   constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -442,16 +507,18 @@ __device__ __forceinline__ void dq_part(bf16* smem, const bf16* Qh, const bf16* 
   const float c = fabsf(scale) * kLog2e;
 
   bf16x8 qf[DS], dof[DS], of[DS];
-  load_frags<D>(qf, Qh, qrow, Nq, g);
-  load_frags<D>(dof, dOh, qrow, Nq, g);
-  load_frags<D>(of, Oh, qrow, Nq, g);
+  load_frags<D>(qf, Qr, qrow, g);
+  load_frags<D>(dof, dOr, qrow, g);
+  load_frags<D>(of, Or, qrow, g);
+  const float lrow = buf_load_f32(Lr, qrow * 4);
+  wait_vmem();
   float dsum = 0.f;
 #pragma unroll
   for (int s = 0; s < DS; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) dsum = fmaf((float)dof[s][e], (float)of[s][e], dsum);
   dsum += swap_halves(dsum);
-  const float l2 = qrow < Nq ? Lh[qrow] * kLog2e : INFINITY;
+  const float l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
   if (neg)
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
@@ -469,8 +536,8 @@ __device__ __forceinline__ void dq_part(bf16* smem, const bf16* Qh, const bf16* 
   RChunks<MT, D, 128> vreg;
 
   auto fetch = [&](int kt) {
-    if (k_role) kreg.load(Kh, kt * MT, Nk, tid);
-    if (v_role) vreg.load(Vh, kt * MT, Nk, tid - 128);
+    if (k_role) kreg.load(Kr, kt * MT, tid);
+    if (v_role) vreg.load(Vr, kt * MT, tid - 128);
   };
   auto stage = [&](bf16* base) {
     if (k_role) {
@@ -498,33 +565,34 @@ __device__ __forceinline__ void dq_part(bf16* smem, const bf16* Qh, const bf16* 
       f32x16 st[NB], dpt[NB];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
+        bf16x8 ka[DS], va[DS];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          ka[s] = lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g);
+          va[s] = lds_frag<D / 8>(sV, 32 * kb + l32, 2 * s + g);
+        }
         st[kb] = zero16();
         dpt[kb] = zero16();
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          st[kb] = mfma32(lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g), qf[s], st[kb]);
-          dpt[kb] = mfma32(lds_frag<D / 8>(sV, 32 * kb + l32, 2 * s + g), dof[s], dpt[kb]);
+          st[kb] = mfma32(ka[s], qf[s], st[kb]);
+          dpt[kb] = mfma32(va[s], dof[s], dpt[kb]);
         }
       }
       // Registers: key n0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query.
-      const bool need_mask = (CAUSAL && n0 + MT - 1 > qw0) || n0 + MT > Nk;
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(st[kb][r], c, -l2));
-          if (need_mask) {
-            const int key = n0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= Nk || (CAUSAL && key > qrow)) p = 0.f;
-          }
-          dpt[kb][r] = p * (dpt[kb][r] - dsum);
-        }
+      if ((CAUSAL && n0 + MT - 1 > qw0) || n0 + MT > Nk)
+        dq_scores<true, NB>(st, dpt, c, l2, dsum, CAUSAL ? qrow - n0 - 4 * g : 1 << 30,
+                            Nk - n0 - 4 * g);
+      else
+        dq_scores<false, NB>(st, dpt, c, l2, dsum, 0, 0);
 #pragma unroll
       for (int s2 = 0; s2 < 2 * NB; ++s2) {
+        bf16x8 kt_[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) kt_[db] = lds_frag<MT / 8>(sKt, 32 * db + l32, 2 * s2 + g);
         const bf16x8 sf = to_bf16x8(dpt[s2 >> 1], 8 * (s2 & 1));
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqt[db] = mfma32(lds_frag<MT / 8>(sKt, 32 * db + l32, 2 * s2 + g), sf, dqt[db]);
+        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(kt_[db], sf, dqt[db]);
       }
     }
     if (more) stage(smem + (buf ^ 1) * C::BUF);
@@ -562,13 +630,16 @@ __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
     r = mn + (idx - 2 * mn);
   }
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
+  const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
+  const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq), dOr = make_rsrc(dO + oq, bq);
+  const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
+  const rsrc_t Lr = make_rsrc(L + (size_t)bh * Nq, (uint32_t)Nq * 4);
   if (kv) {
-    dkdv_part<D, CAUSAL>(smem, Q + oq, K + ok, V + ok, O + oq, L + (size_t)bh * Nq, dO + oq,
-                         dK + ok, dV + ok, r * 128, Nq, Nk, scale, neg);
+    dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, r * 128, Nq, Nk, scale,
+                         neg);
   } else {
     const int it = CAUSAL ? nqw - 1 - r : r;
-    dq_part<D, CAUSAL>(smem, Q + oq, K + ok, V + ok, O + oq, L + (size_t)bh * Nq, dO + oq,
-                       dQ + oq, it * 128, Nq, Nk, scale, neg);
+    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
   }
 }
 

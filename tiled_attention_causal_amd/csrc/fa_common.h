@@ -17,6 +17,26 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Buffer resource over `bytes` bytes at `base` (gfx9 raw buffer: stride 0, dword3 0x00020000).
+// Loads whose bytes fall past `bytes` return zeros, which is how ragged tiles are padded:
+// no branch, no select.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+// Wait until every outstanding vector-memory load of this wave has returned.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
 // Fragment layout with g = lane / 32:
 //   A: lane holds row (lane % 32), k = 8g .. 8g+7;  B: lane holds column (lane % 32), same k;
