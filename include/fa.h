@@ -39,7 +39,7 @@
  *   FA_ERROR_LAUNCH_FAILED  the HIP runtime rejected a kernel launch.
  * No C++ exception crosses this interface.
  *
- * Limits: Nq, Nk <= 2^24, B*H <= 2^31 - 1 and B*H*(ceil(Nq/32) + ceil(Nk/32)) < 2^24
+ * Limits: Nq, Nk <= 2^22, B*H <= 2^31 - 1 and B*H*(ceil(Nq/32) + ceil(Nk/32)) < 2^24
  * (launch grids count work-items in 32 bits). Any positive Nq, Nk is accepted (ragged
  * tiles are masked); Nq != Nk is allowed. B*H*Nq == 0 makes fa_forward a no-op; in
  * fa_backward, Nq == 0 with Nk > 0 writes dK = dV = 0.

@@ -83,7 +83,7 @@ def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P,
     (dict(d=48), 2), (dict(d=256), 2), (dict(d=0), 1), (dict(d=-64), 1),
     (dict(B=-1), 1), (dict(H=-1), 1), (dict(Nq=-1), 1), (dict(Nk=-5), 1),
     (dict(Nk=0), 1),
-    (dict(Nq=(1 << 24) + 1), 2), (dict(B=1 << 20, H=1 << 12), 2),
+    (dict(Nq=(1 << 22) + 1), 2), (dict(Nk=(1 << 22) + 1), 2), (dict(B=1 << 20, H=1 << 12), 2),
     (dict(scale=math.inf), 1), (dict(scale=math.nan), 1),
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
     (dict(lse=None), 1), (dict(q=BAD), 1), (dict(o=BAD), 1),

@@ -8,7 +8,8 @@
 
 namespace {
 
-constexpr int64_t kMaxN = int64_t(1) << 24;
+// Per-head buffers are addressed with 32-bit byte offsets: N * d * 2 < 2^31 for d <= 128.
+constexpr int64_t kMaxN = int64_t(1) << 22;
 constexpr int64_t kMaxBH = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxGroups = (int64_t(1) << 24) - 1;
 

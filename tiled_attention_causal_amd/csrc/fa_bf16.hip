@@ -1,6 +1,6 @@
 // bf16 attention forward and backward for gfx950 (CDNA4): 32x32x16 bf16 MFMA with fp32
-// accumulation, K/V (forward), Q/dO (dK/dV pass) and K/V (dQ pass) tiles staged through
-// LDS, online softmax in registers.
+// accumulation; streaming tiles land in LDS straight from HBM (buffer loads with the LDS
+// destination) and transposed MFMA operands are read with ds_read_b64_tr_b16.
 //
 // Method: "Systems and Parallelism" (CS336 field map, A2), section 1.2-1.3.
 //   forward  (problem flash_forward): each workgroup owns one query tile and walks the key
@@ -19,13 +19,18 @@
 // them as MFMA B operands, so every score tile comes out with one stationary row per lane
 // (lane % 32) and the moving rows spread over the 16 accumulator registers. Row statistics
 // are then per lane, plus one exchange with lane ^ 32. The second product of each pass
-// (P V, P^T dO, dS^T Q, dS K) takes the score registers directly as its B operand; the LDS
-// operand for it is stored transposed with the row permutation of tpos().
+// (P V, P^T dO, dS^T Q, dS K) takes the score registers directly as its B operand and reads
+// its LDS operand transposed (Tile::tfrag).
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   u32x4 u = __builtin_bit_cast(u32x4, x);
@@ -33,71 +38,66 @@ __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ float lo_f(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
-__device__ __forceinline__ float hi_f(uint32_t x) {
-  return __builtin_bit_cast(float, x & 0xFFFF0000u);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 8 rows (those of transposed chunk kc) x 4 columns of an [MT x D] bf16 tile.
-template <int MT, int D>
-struct TUnit {
-  static constexpr int N = (MT / 8) * (D / 4);
-  u32x2 r[8];
+// Wave index as a scalar, so LDS destinations of the direct loads stay uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 
-  __device__ __forceinline__ void load(rsrc_t head, int row0, int u) {
-    const int d4 = u % (D / 4), kc = u / (D / 4);
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at dst + 16 i.
+__device__ __forceinline__ void dma16(rsrc_t src, uint32_t byte_off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 16, byte_off, 0, 0, 0);
+}
+// 4 bytes per lane (lane i's word lands at dst + 4 i).
+__device__ __forceinline__ void dma4(rsrc_t src, uint32_t byte_off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 4, byte_off, 0, 0, 0);
+}
+
+// Row-major R x C bf16 LDS tile with 16-byte chunks XOR-swizzled by row (swz in fa_common.h).
+template <int R, int C>
+struct Tile {
+  static constexpr int NCH = C / 8;
+  static constexpr int ELEMS = R * C;
+  static constexpr int NKIB = ELEMS * 2 / 1024;  // one wave-wide direct load moves 1 KiB
+  static_assert(ELEMS * 2 % 1024 == 0, "tile must be a whole number of KiB");
+
+  // Rows [row0, row0 + R) of a head with C columns, spread over NW waves. LDS chunk p holds
+  // the global chunk whose swizzled position is p; rows past the head's end read as zeros.
+  template <int NW>
+  __device__ __forceinline__ static void load(rsrc_t src, int row0, bf16* t, int w, int lane) {
+    constexpr int M = NCH < 8 ? NCH - 1 : 7;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      r[e] = buf_load8(head, ((row0 + chunk_row(kc, e)) * D + 4 * d4) * 2);
-  }
-  // Row-major copy: tile[MT][D].
-  __device__ __forceinline__ void store_rows(bf16* tile, int u) const {
-    const int d4 = u % (D / 4), kc = u / (D / 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<u32x2*>(tile + swz<D / 8>(chunk_row(kc, e), d4 >> 1) + 4 * (d4 & 1)) =
-          r[e];
-  }
-  // Transposed copy: tile[d][tpos(row)], MT columns per row.
-  __device__ __forceinline__ void store_trans(bf16* tile, int u) const {
-    const int d4 = u % (D / 4), kc = u / (D / 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = (i & 2) ? r[2 * j].y : r[2 * j].x;
-        const uint32_t b = (i & 2) ? r[2 * j + 1].y : r[2 * j + 1].x;
-        v[j] = (i & 1) ? pack_hi(a, b) : pack_lo(a, b);
+    for (int i = 0; i < (NKIB + NW - 1) / NW; ++i) {
+      const int blk = w + i * NW;
+      if (NKIB % NW == 0 || blk < NKIB) {
+        const int p = blk * 64 + lane;
+        const int row = p / NCH, cp = p % NCH;
+        const int gc = cp ^ ((row ^ (row >> 3)) & M);
+        dma16(src, (uint32_t)(((row0 + row) * C + gc * 8) * 2), t + blk * 512);
       }
-      *reinterpret_cast<u32x4*>(tile + swz<MT / 8>(4 * d4 + i, kc)) = v;
     }
   }
-};
-
-// Row-major [MT x D] tile moved as 16-byte chunks by NT threads.
-template <int MT, int D, int NT>
-struct RChunks {
-  static constexpr int NC = MT * D / 8;
-  static constexpr int PER = (NC + NT - 1) / NT;
-  u32x4 r[PER];
-
-  __device__ __forceinline__ void load(rsrc_t head, int row0, int t) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = t + p * NT;
-      if (NC % NT == 0 || c < NC)
-        r[p] = buf_load16(head, ((row0 + c / (D / 8)) * D + 8 * (c % (D / 8))) * 2);
-    }
+  // Operand with k along columns: lane takes row r, columns 8c .. 8c+7.
+  __device__ __forceinline__ static bf16x8 frag(const bf16* t, int r, int c) {
+    return lds_frag<NCH>(t, r, c);
   }
-  __device__ __forceinline__ void store(bf16* tile, int t) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = t + p * NT;
-      if (c < NC) *reinterpret_cast<u32x4*>(tile + swz<D / 8>(c / (D / 8), c % (D / 8))) = r[p];
-    }
+  // Transposed operand: lane l takes column cbase + l%32 and the eight rows
+  // kbase + 8h + 4g + j (h = 0, 1; j = 0..3; g = l/32) in element order 4h + j, which is the
+  // row order of an MFMA C fragment's 16-row step. Each ds_read_b64_tr_b16 gathers, inside
+  // a 16-lane group, the 4 x 4 block that lane 4a + b's column needs: lane k of the group
+  // reads row base + k/4, columns 4(k%4) .. +3, and receives column 4a+b of rows base..+3.
+  __device__ __forceinline__ static bf16x8 tfrag(const bf16* t, int cbase, int kbase, int lane) {
+    const int g = lane >> 5, s = (lane >> 4) & 1, k = lane & 15;
+    int col = cbase + 16 * s + 4 * (k & 3);
+    if constexpr (C < 32) col &= C - 1;  // d = 16: the unused half-block re-reads valid columns
+    const int row = kbase + 4 * g + (k >> 2);
+    const bf16* p0 = t + swz<NCH>(row, col >> 3) + (col & 7);
+    const bf16* p1 = t + swz<NCH>(row + 8, col >> 3) + (col & 7);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
+    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, ab);
   }
 };
 
@@ -112,7 +112,8 @@ __device__ __forceinline__ void load_frags(bf16x8 (&f)[D / 16], rsrc_t head, int
 // Store a transposed 32-wide output block: lane owns row `row`; register r of block db holds
 // column 32db + 8(r/4) + 4g + r%4.
 template <int D>
-__device__ __forceinline__ void store_rows_from_acc(bf16* out_row, const f32x16 (&acc)[(D + 31) / 32],
+__device__ __forceinline__ void store_rows_from_acc(bf16* out_row,
+                                                    const f32x16 (&acc)[(D + 31) / 32],
                                                     float mul, int g) {
 #pragma unroll
   for (int db = 0; db < (D + 31) / 32; ++db)
@@ -185,10 +186,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
                                                   bf16* __restrict__ O, float* __restrict__ Lout,
                                                   int Nq, int Nk, float scale, int neg) {
   constexpr int BQ = 128, BK = 64;
-  constexpr int DS = D / 16, DB = (D + 31) / 32, DP = 32 * DB;
-  constexpr int KT = BK * D, VT = DP * BK, BUF = KT + VT;
-  constexpr int NVU = TUnit<BK, D>::N;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
+  using KTile = Tile<BK, D>;
+  constexpr int BUF = 2 * KTile::ELEMS;  // K then V, both row-major
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * BUF];
 
   const int nqt = (Nq + BQ - 1) / BQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   const rsrc_t Kr = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
   const rsrc_t Vr = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
   const float cs = fabsf(scale);
@@ -210,7 +211,6 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 
   bf16x8 qf[DS];
   load_frags<D>(qf, Qr, qrow, g);
-  wait_vmem();  // keeps the loop's own prefetch waits exact
   if (neg)
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
@@ -220,32 +220,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   for (int db = 0; db < DB; ++db) o[db] = zero16();
   float m = 0.f, l = 0.f;
 
-  RChunks<BK, D, 256> kreg;
-  TUnit<BK, D> vreg;
-  kreg.load(Kr, 0, tid);
-  if (tid < NVU) vreg.load(Vr, 0, tid);
-  kreg.store(smem, tid);
-  if (tid < NVU) vreg.store_trans(smem + KT, tid);
+  KTile::template load<4>(Kr, 0, smem, w, lane);
+  KTile::template load<4>(Vr, 0, smem + KTile::ELEMS, w, lane);
+  wait_vmem();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      kreg.load(Kr, (kt + 1) * BK, tid);
-      if (tid < NVU) vreg.load(Vr, (kt + 1) * BK, tid);
+    if (kt + 1 < nkt) {
+      bf16* nb = smem + (buf ^ 1) * BUF;
+      KTile::template load<4>(Kr, (kt + 1) * BK, nb, w, lane);
+      KTile::template load<4>(Vr, (kt + 1) * BK, nb + KTile::ELEMS, w, lane);
     }
     const int k0 = kt * BK;
     const bool active = qw0 < Nq && (!CAUSAL || k0 <= qw0 + 31);
     if (active) {
       const bf16* sK = smem + buf * BUF;
-      const bf16* sV = sK + KT;
-      // All K fragments of the tile first, so the LDS latency is paid once.
+      const bf16* sV = sK + KTile::ELEMS;
       bf16x8 kfr[2][DS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < DS; ++s) kfr[kb][s] = lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g);
+        for (int s = 0; s < DS; ++s) kfr[kb][s] = KTile::frag(sK, 32 * kb + l32, 2 * s + g);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -257,7 +253,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vfr[u][db] = lds_frag<BK / 8>(sV, 32 * db + l32, 2 * u + g);
+        for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(sV, 32 * db, 16 * u, lane);
       // Score registers: key k0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query. Only
       // tiles that straddle the diagonal or the ragged end of K compare indices; masked
       // entries are left out of the row max and zeroed after the exponential, which stays
@@ -276,11 +272,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
         for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf, o[db]);
       }
     }
-    if (more) {
-      bf16* nbuf = smem + (buf ^ 1) * BUF;
-      kreg.store(nbuf, tid);
-      if (tid < NVU) vreg.store_trans(nbuf + KT, tid);
-    }
+    wait_vmem();
     __syncthreads();
   }
 
@@ -337,16 +329,31 @@ template <int D>
 struct BwdCfg {
   static constexpr int MT = D >= 128 ? 32 : 64;  // moving-tile rows
   static constexpr int NB = MT / 32;
-  static constexpr int DS = D / 16, DB = (D + 31) / 32, DP = 32 * DB;
-  static constexpr int T_RM = MT * D;   // row-major tile, elements
-  static constexpr int T_TR = DP * MT;  // transposed tile, elements
-  // dK/dV staging: Q, dO (row-major), Q^T, dO^T, then L*log2e and D as MT floats each.
-  static constexpr int BUF_KV = 2 * T_RM + 2 * T_TR + 4 * MT;
-  // dQ staging: K, V (row-major), K^T.
-  static constexpr int BUF_Q = 2 * T_RM + T_TR;
+  static constexpr int DS = D / 16, DB = (D + 31) / 32;
+  using MTile = Tile<MT, D>;
+  static constexpr int T = MTile::ELEMS;
+  // dK/dV staging: Q, dO, O (row-major), then L (-> L log2e) and D, 64 floats each.
+  static constexpr int BUF_KV = 3 * T + 2 * 64 * 2;
+  // dQ staging: K, V (row-major).
+  static constexpr int BUF_Q = 2 * T;
   static constexpr int BUF = BUF_KV > BUF_Q ? BUF_KV : BUF_Q;
-  static constexpr int NU = TUnit<MT, D>::N;  // <= 128
+  // D = rowsum(dO o O) over the staged tile: CPT 16-byte chunks per thread, TPR threads per
+  // row.
+  static constexpr int NCH = D / 8;
+  static constexpr int CPT = MT * NCH >= 512 ? 2 : 1;
+  static constexpr int TPR = NCH / CPT;
 };
+
+__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__builtin_bit_cast(float, a[i] << 16), __builtin_bit_cast(float, b[i] << 16),
+               acc);
+    acc = fmaf(__builtin_bit_cast(float, a[i] & 0xFFFF0000u),
+               __builtin_bit_cast(float, b[i] & 0xFFFF0000u), acc);
+  }
+  return acc;
+}
 
 // dK, dV for the 128 keys starting at k0 of one head.
 template <int D, bool CAUSAL>
@@ -354,8 +361,9 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
                                           rsrc_t Lr, rsrc_t dOr, bf16* dKh, bf16* dVh, int k0,
                                           int Nq, int Nk, float scale, int neg) {
   using C = BwdCfg<D>;
-  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  using MTile = typename C::MTile;
+  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB, T = C::T;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int kw0 = k0 + 32 * w;
   const int krow = kw0 + l32;
   const float c = fabsf(scale) * kLog2e;
@@ -363,7 +371,6 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   bf16x8 kf[DS], vf[DS];
   load_frags<D>(kf, Kr, krow, g);
   load_frags<D>(vf, Vr, krow, g);
-  wait_vmem();
   if (neg)
 #pragma unroll
     for (int s = 0; s < DS; ++s) kf[s] = negate(kf[s]);
@@ -378,80 +385,38 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   const int nmt = (Nq + MT - 1) / MT;
   const int mt0 = CAUSAL ? k0 / MT : 0;
 
-  // Staging roles: threads [0, NU) move Q; threads [128, 128 + NU) move dO and O (for D);
-  // threads [0, MT) also fetch L.
-  const bool q_role = tid < C::NU;
-  const bool do_role = tid >= 128 && tid - 128 < C::NU;
-  const int u = do_role ? tid - 128 : tid;
-  TUnit<MT, D> qreg, doreg, oreg;
-  float lreg = 0.f;
-
-  auto fetch = [&](int mt) {
+  auto fetch = [&](int mt, bf16* base) {
     const int m0 = mt * MT;
-    if (q_role) qreg.load(Qr, m0, u);
-    if (do_role) {
-      doreg.load(dOr, m0, u);
-      oreg.load(Or, m0, u);
-    }
-    if (tid < MT) lreg = buf_load_f32(Lr, (m0 + tid) * 4);
-  };
-  auto stage = [&](int mt, bf16* base) {
-    const int m0 = mt * MT;
-    bf16* sQ = base;
-    bf16* sdO = base + C::T_RM;
-    bf16* sQt = base + 2 * C::T_RM;
-    bf16* sdOt = sQt + C::T_TR;
-    float* sL2 = reinterpret_cast<float*>(sdOt + C::T_TR);
-    float* sD = sL2 + MT;
-    if (q_role) {
-      qreg.store_rows(sQ, u);
-      qreg.store_trans(sQt, u);
-    }
-    if (do_role) {
-      doreg.store_rows(sdO, u);
-      doreg.store_trans(sdOt, u);
-      const int d4 = u % (D / 4), kc = u / (D / 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const u32x2 a = doreg.r[e], b = oreg.r[e];
-        float pd = lo_f(a.x) * lo_f(b.x);
-        pd = fmaf(hi_f(a.x), hi_f(b.x), pd);
-        pd = fmaf(lo_f(a.y), lo_f(b.y), pd);
-        pd = fmaf(hi_f(a.y), hi_f(b.y), pd);
-        pd = group_sum<D / 4>(pd);
-        if (d4 == 0) sD[chunk_row(kc, e)] = pd;
-      }
-    }
-    if (tid < MT) sL2[tid] = m0 + tid < Nq ? lreg * kLog2e : INFINITY;
+    MTile::template load<4>(Qr, m0, base, w, lane);
+    MTile::template load<4>(dOr, m0, base + T, w, lane);
+    MTile::template load<4>(Or, m0, base + 2 * T, w, lane);
+    if (w == 0) dma4(Lr, (uint32_t)(m0 + lane) * 4, base + 3 * T);
   };
 
-  if (mt0 < nmt) {
-    fetch(mt0);
-    stage(mt0, smem);
-  }
+  if (mt0 < nmt) fetch(mt0, smem);
+  wait_vmem();
   __syncthreads();
   for (int mt = mt0; mt < nmt; ++mt) {
     const int buf = (mt - mt0) & 1;
-    const bool more = mt + 1 < nmt;
-    if (more) fetch(mt + 1);
+    if (mt + 1 < nmt) fetch(mt + 1, smem + (buf ^ 1) * C::BUF);
     const int m0 = mt * MT;
+    bf16* base = smem + buf * C::BUF;
+    const bf16* sQ = base;
+    const bf16* sdO = base + T;
+    const bf16* sO = base + 2 * T;
+    float* sL2 = reinterpret_cast<float*>(base + 3 * T);
+    float* sD = sL2 + 64;
     const bool active = kw0 < Nk && (!CAUSAL || m0 + MT - 1 >= kw0);
+
+    f32x16 sp[NB], dp[NB];
     if (active) {
-      const bf16* base = smem + buf * C::BUF;
-      const bf16* sQ = base;
-      const bf16* sdO = base + C::T_RM;
-      const bf16* sQt = base + 2 * C::T_RM;
-      const bf16* sdOt = sQt + C::T_TR;
-      const float* sL2 = reinterpret_cast<const float*>(sdOt + C::T_TR);
-      const float* sD = sL2 + MT;
-      f32x16 sp[NB], dp[NB];
 #pragma unroll
       for (int qb = 0; qb < NB; ++qb) {
         bf16x8 qa[DS], da[DS];
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          qa[s] = lds_frag<D / 8>(sQ, 32 * qb + l32, 2 * s + g);
-          da[s] = lds_frag<D / 8>(sdO, 32 * qb + l32, 2 * s + g);
+          qa[s] = MTile::frag(sQ, 32 * qb + l32, 2 * s + g);
+          da[s] = MTile::frag(sdO, 32 * qb + l32, 2 * s + g);
         }
         sp[qb] = zero16();
         dp[qb] = zero16();
@@ -461,6 +426,28 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
           dp[qb] = mfma32(da[s], vf[s], dp[qb]);
         }
       }
+    }
+    // D and L log2e for the tile's rows, while the MFMAs above run.
+    {
+      const int row = tid / C::TPR, part = tid % C::TPR;
+      float dsum = 0.f;
+      if (row < MT) {
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+          const int ch = part * C::CPT + i;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sdO + swz<C::NCH>(row, ch));
+          const u32x4 b = *reinterpret_cast<const u32x4*>(sO + swz<C::NCH>(row, ch));
+          dsum = dot_bf16x8(a, b, dsum);
+        }
+      }
+      dsum = group_sum<C::TPR>(dsum);
+      if (row < MT && part == 0) {
+        sD[row] = dsum;
+        sL2[row] = m0 + row < Nq ? sL2[row] * kLog2e : INFINITY;
+      }
+    }
+    __syncthreads();
+    if (active) {
       // Registers: query m0 + 32qb + 8(r/4) + 4g + r%4 against this lane's key; the key is
       // visible iff query >= key, i.e. offset 32qb + 8(r/4) + r%4 >= krow - m0 - 4g.
       if (CAUSAL && m0 < kw0 + 31)
@@ -472,8 +459,8 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
         bf16x8 ofr[DB], qfr[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          ofr[db] = lds_frag<MT / 8>(sdOt, 32 * db + l32, 2 * st + g);
-          qfr[db] = lds_frag<MT / 8>(sQt, 32 * db + l32, 2 * st + g);
+          ofr[db] = MTile::tfrag(sdO, 32 * db, 16 * st, lane);
+          qfr[db] = MTile::tfrag(sQ, 32 * db, 16 * st, lane);
         }
         const bf16x8 pf = to_bf16x8(sp[st >> 1], 8 * (st & 1));
         const bf16x8 sf = to_bf16x8(dp[st >> 1], 8 * (st & 1));
@@ -484,7 +471,7 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
         }
       }
     }
-    if (more) stage(mt + 1, smem + (buf ^ 1) * C::BUF);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -500,8 +487,9 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
                                         rsrc_t Lr, rsrc_t dOr, bf16* dQh, int q0, int Nq, int Nk,
                                         float scale, int neg) {
   using C = BwdCfg<D>;
-  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  using MTile = typename C::MTile;
+  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB, T = C::T;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
   const float c = fabsf(scale) * kLog2e;
@@ -530,46 +518,30 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
   int nkt = (Nk + MT - 1) / MT;
   if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / MT + 1);
 
-  const bool k_role = tid < C::NU;
-  const bool v_role = tid >= 128;
-  TUnit<MT, D> kreg;
-  RChunks<MT, D, 128> vreg;
-
-  auto fetch = [&](int kt) {
-    if (k_role) kreg.load(Kr, kt * MT, tid);
-    if (v_role) vreg.load(Vr, kt * MT, tid - 128);
-  };
-  auto stage = [&](bf16* base) {
-    if (k_role) {
-      kreg.store_rows(base, tid);
-      kreg.store_trans(base + 2 * C::T_RM, tid);
-    }
-    if (v_role) vreg.store(base + C::T_RM, tid - 128);
+  auto fetch = [&](int kt, bf16* base) {
+    MTile::template load<4>(Kr, kt * MT, base, w, lane);
+    MTile::template load<4>(Vr, kt * MT, base + T, w, lane);
   };
 
-  if (nkt > 0) {
-    fetch(0);
-    stage(smem);
-  }
+  if (nkt > 0) fetch(0, smem);
+  wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) fetch(kt + 1);
+    if (kt + 1 < nkt) fetch(kt + 1, smem + (buf ^ 1) * C::BUF);
     const int n0 = kt * MT;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
     if (active) {
       const bf16* sK = smem + buf * C::BUF;
-      const bf16* sV = sK + C::T_RM;
-      const bf16* sKt = sK + 2 * C::T_RM;
+      const bf16* sV = sK + T;
       f32x16 st[NB], dpt[NB];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
         bf16x8 ka[DS], va[DS];
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          ka[s] = lds_frag<D / 8>(sK, 32 * kb + l32, 2 * s + g);
-          va[s] = lds_frag<D / 8>(sV, 32 * kb + l32, 2 * s + g);
+          ka[s] = MTile::frag(sK, 32 * kb + l32, 2 * s + g);
+          va[s] = MTile::frag(sV, 32 * kb + l32, 2 * s + g);
         }
         st[kb] = zero16();
         dpt[kb] = zero16();
@@ -587,23 +559,25 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
         dq_scores<false, NB>(st, dpt, c, l2, dsum, 0, 0);
 #pragma unroll
       for (int s2 = 0; s2 < 2 * NB; ++s2) {
-        bf16x8 kt_[DB];
+        bf16x8 ktf[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) kt_[db] = lds_frag<MT / 8>(sKt, 32 * db + l32, 2 * s2 + g);
+        for (int db = 0; db < DB; ++db) ktf[db] = MTile::tfrag(sK, 32 * db, 16 * s2, lane);
         const bf16x8 sf = to_bf16x8(dpt[s2 >> 1], 8 * (s2 & 1));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(kt_[db], sf, dqt[db]);
+        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(ktf[db], sf, dqt[db]);
       }
     }
-    if (more) stage(smem + (buf ^ 1) * C::BUF);
+    wait_vmem();
     __syncthreads();
   }
 
   if (qrow < Nq) store_rows_from_acc<D>(dQh + (size_t)qrow * D, dqt, scale, g);
 }
 
-// One launch for the whole backward: per head, workgroups alternate between a dK/dV key
-// tile (fewest-visible-queries last) and a dQ query tile (most-visible-keys first).
+// One launch for the whole backward. Per head the workgroups run the dK/dV key tiles in
+// order (most visible queries first) and then the dQ query tiles in order (fewest visible
+// keys first), so that the k-th dK/dV tile and the k-th dQ tile, which are dispatched one
+// head-width apart, carry complementary amounts of causal work.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
@@ -614,32 +588,23 @@ __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
                                                   bf16* __restrict__ dQ, bf16* __restrict__ dK,
                                                   bf16* __restrict__ dV, int Nq, int Nk,
                                                   float scale, int neg) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BwdCfg<D>::BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * BwdCfg<D>::BUF];
   const int nkv = (Nk + 127) / 128, nqw = (Nq + 127) / 128;
   const int per_head = nkv + nqw;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = lid / per_head, idx = lid % per_head;
-  const int mn = min(nkv, nqw);
-  bool kv;
-  int r;
-  if (idx < 2 * mn) {
-    kv = (idx & 1) == 0;
-    r = idx >> 1;
-  } else {
-    kv = nkv > nqw;
-    r = mn + (idx - 2 * mn);
-  }
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
   const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
-  const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq), dOr = make_rsrc(dO + oq, bq);
+  const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq);
+  const rsrc_t dOr = make_rsrc(dO + oq, bq);
   const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
   const rsrc_t Lr = make_rsrc(L + (size_t)bh * Nq, (uint32_t)Nq * 4);
-  if (kv) {
-    dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, r * 128, Nq, Nk, scale,
-                         neg);
+  if (idx < nkv) {
+    dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, idx * 128, Nq, Nk,
+                         scale, neg);
   } else {
-    const int it = CAUSAL ? nqw - 1 - r : r;
-    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
+    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, (idx - nkv) * 128, Nq, Nk,
+                       scale, neg);
   }
 }
 
