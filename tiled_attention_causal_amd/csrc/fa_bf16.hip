@@ -27,6 +27,8 @@
 namespace fa {
 namespace {
 
+constexpr int kNumCUs = 256;  // MI355X
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -225,18 +227,27 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   wait_vmem();
   __syncthreads();
 
+  // Each iteration issues its transposed V reads before the next tile's direct loads: the
+  // compiler cannot tell that they do not alias and would otherwise wait for those loads (the
+  // full memory latency) before the reads. Plain LDS reads do not have this problem.
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
+    const int k0 = kt * BK;
+    const bool active = qw0 < Nq && (!CAUSAL || k0 <= qw0 + 31);
+    const bf16* sK = smem + buf * BUF;
+    const bf16* sV = sK + KTile::ELEMS;
+    bf16x8 vfr[4][DB];
+    if (active)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(sV, 32 * db, 16 * u, lane);
     if (kt + 1 < nkt) {
       bf16* nb = smem + (buf ^ 1) * BUF;
       KTile::template load<4>(Kr, (kt + 1) * BK, nb, w, lane);
       KTile::template load<4>(Vr, (kt + 1) * BK, nb + KTile::ELEMS, w, lane);
     }
-    const int k0 = kt * BK;
-    const bool active = qw0 < Nq && (!CAUSAL || k0 <= qw0 + 31);
     if (active) {
-      const bf16* sK = smem + buf * BUF;
-      const bf16* sV = sK + KTile::ELEMS;
       bf16x8 kfr[2][DS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -249,11 +260,6 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 #pragma unroll
         for (int s = 0; s < DS; ++s) sacc[kb] = mfma32(kfr[kb][s], qf[s], sacc[kb]);
       }
-      bf16x8 vfr[4][DB];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(sV, 32 * db, 16 * u, lane);
       // Score registers: key k0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query. Only
       // tiles that straddle the diagonal or the ragged end of K compare indices; masked
       // entries are left out of the row max and zeroed after the exponential, which stays
@@ -283,6 +289,168 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   }
 }
 
+// Causal forward with complementary tile pairing, for Nq = Nk = N, N % 128 == 0.
+//
+// With 64-row query tiles and 64-key tiles, query tile t sees key tiles 0..t, so tile t
+// costs t + 1 steps and a plain one-tile-per-workgroup grid finishes when its last tile,
+// N/64 steps long, does. Here each workgroup takes tiles A = T-1-i and B = i (T = N/64):
+// T + 1 steps together, split evenly between its two wave pairs. Pair 0 runs A over key
+// tiles [0, s); pair 1 runs B over [0, i+1) and then A over [s, T-i), with s = T/2 + 1.
+// Both pairs step in lockstep (one barrier per step, each with its own K/V stream), and at
+// the end pair 1 hands its partial (m, l, O) for A to pair 0 through LDS, which merges the
+// two with the same rescale the online softmax uses between key tiles.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg) {
+  constexpr int BK = 64;
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
+  using KTile = Tile<BK, D>;
+  constexpr int KT = KTile::ELEMS;
+  // Two statically distinct double buffers, so a step's direct loads into one provably do
+  // not alias its LDS reads from the other. Index: [pair][K or V].
+  __shared__ __attribute__((aligned(1024))) bf16 sb0[2][2][KT];
+  __shared__ __attribute__((aligned(1024))) bf16 sb1[2][2][KT];
+
+  const int T = N / 64;
+  const int half = T / 2;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / half, i = lid % half;
+  const int tA = T - 1 - i, tB = i, s = half + 1;
+  const rsrc_t Qr = make_rsrc(Q + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Kr = make_rsrc(K + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Vr = make_rsrc(V + (size_t)bh * N * D, (uint32_t)N * D * 2);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int pr = w >> 1, wp = w & 1;  // pair, wave within pair
+  const float cs = fabsf(scale);
+  const float c = cs * kLog2e;
+
+  // Steps of this pair: step n works on query tile qt(n) and key tile kt(n).
+  //   pair 0: n in [0, s):           A, key tile n
+  //   pair 1: n in [0, i+1):         B, key tile n;  n in [i+1, T-s+1): A, key tile n - (i+1) + s
+  const int nsteps = pr == 0 ? s : T + 1 - s;
+  auto qt_of = [&](int n) { return (pr == 0 || n > tB) ? tA : tB; };
+  auto kt_of = [&](int n) { return (pr == 0 || n <= tB) ? n : n - (tB + 1) + s; };
+
+  // Query fragments for both tiles this wave may own (rows 64 qt + 32 wp + lane % 32).
+  bf16x8 qfA[DS], qfB[DS];
+  load_frags<D>(qfA, Qr, 64 * tA + 32 * wp + l32, g);
+  load_frags<D>(qfB, Qr, 64 * tB + 32 * wp + l32, g);
+  if (neg)
+#pragma unroll
+    for (int q = 0; q < DS; ++q) {
+      qfA[q] = negate(qfA[q]);
+      qfB[q] = negate(qfB[q]);
+    }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  float m = 0.f, l = 0.f;
+
+  auto fetch = [&](int n, bf16 (*dst)[KT]) {
+    const int k0 = kt_of(n) * BK;
+    KTile::template load<2>(Kr, k0, dst[0], wp, lane);
+    KTile::template load<2>(Vr, k0, dst[1], wp, lane);
+  };
+  auto finish_B = [&]() {  // pair 1, after B's last key tile: B is complete
+    const float lt = l + swap_halves(l);
+    const int row = 64 * tB + 32 * wp + l32;
+    store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
+    if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = zero16();
+    m = 0.f;
+    l = 0.f;
+  };
+  auto step = [&](int n, const bf16 (*cur)[KT], bf16 (*nxt)[KT]) {
+    // The transposed V reads come before the next tile's direct loads: the compiler cannot
+    // tell that they do not alias and would otherwise wait for those loads to land first.
+    bf16x8 vfr[4][DB];
+    if (n < nsteps)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(cur[1], 32 * db, 16 * u, lane);
+    if (n + 1 < nsteps) fetch(n + 1, nxt);
+    if (n < nsteps) {
+      const int qt = qt_of(n), kt = kt_of(n);
+      const bool first = pr == 0 ? n == 0 : (n == 0 || n == tB + 1);
+      const int qrow = 64 * qt + 32 * wp + l32;
+      const int k0 = kt * BK;
+      const bf16x8(&qf)[DS] = qt == tA ? qfA : qfB;
+      bf16x8 kfr[2][DS];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(cur[0], 32 * kb + l32, 2 * q + g);
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = zero16();
+#pragma unroll
+        for (int q = 0; q < DS; ++q) sacc[kb] = mfma32(kfr[kb][q], qf[q], sacc[kb]);
+      }
+      if (kt == qt)  // the diagonal tile: key offset <= query offset
+        softmax_tile<true>(sacc, m, l, o, c, first, qrow - k0 - 4 * g, 1 << 30);
+      else
+        softmax_tile<false>(sacc, m, l, o, c, first, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf, o[db]);
+      }
+      if (pr == 1 && n == tB) finish_B();
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  fetch(0, sb0[pr]);
+  wait_vmem();
+  __syncthreads();
+  for (int n = 0; n < s; n += 2) {
+    step(n, sb0[pr], sb1[pr]);
+    if (n + 1 < s) step(n + 1, sb1[pr], sb0[pr]);
+  }
+
+  // Merge A: pair 1 holds A over key tiles [s, T - i) unless that range is empty.
+  const bool p1_has_A = T - tB > s;
+  constexpr int XS = 16 * DB + 2;  // per lane: O block(s), m, l
+  static_assert(2 * 64 * XS * sizeof(float) <= sizeof(sb0), "merge area must fit in sb0");
+  float* xf = reinterpret_cast<float*>(&sb0[0][0][0]);  // 2 waves x 64 lanes x XS
+  if (pr == 1 && p1_has_A) {
+    float* x = xf + (wp * 64 + lane) * XS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[16 * db + r] = o[db][r];
+    x[16 * DB] = m;
+    x[16 * DB + 1] = l;
+  }
+  __syncthreads();
+  if (pr == 0) {
+    if (p1_has_A) {
+      const float* x = xf + (wp * 64 + lane) * XS;
+      const float m1 = x[16 * DB], l1 = x[16 * DB + 1];
+      const float mm = fmaxf(m, m1);
+      const float a0 = fast_exp2((m - mm) * c), a1 = fast_exp2((m1 - mm) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + x[16 * db + r] * a1;
+      l = l * a0 + l1 * a1;
+      m = mm;
+    }
+    const float lt = l + swap_halves(l);
+    const int row = 64 * tA + 32 * wp + l32;
+    store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
+    if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
+  }
+}
+
 // ----------------------------------------------------------------------------- backward
 
 // dK/dV pass: P = exp2(S c - L log2e) and dS = P (dP - D) in place, for score registers laid
@@ -290,23 +458,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 // Masked (query < key) entries get P = dS = 0.
 template <bool MASKED, int NB>
 __device__ __forceinline__ void dkdv_scores(f32x16 (&sp)[NB], f32x16 (&dp)[NB],
-                                            const float* sL2, const float* sD, float c, int g,
-                                            int lim) {
+                                            const f32x4 (&l4)[NB][4], const f32x4 (&d4)[NB][4],
+                                            float c, int lim) {
 #pragma unroll
   for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 32 * qb + 8 * j + 4 * g);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * qb + 8 * j + 4 * g);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * j + i;
-        float p = fast_exp2(fmaf(sp[qb][r], c, -l4[i]));
+        float p = fast_exp2(fmaf(sp[qb][r], c, -l4[qb][j][i]));
         if (MASKED && 32 * qb + 8 * j + i < lim) p = 0.f;
         sp[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - d4[i]);
+        dp[qb][r] = p * (dp[qb][r] - d4[qb][j][i]);
       }
-    }
 }
 
 // dQ pass: the same for lane = query and register r of block kb = key offset
@@ -327,7 +492,7 @@ __device__ __forceinline__ void dq_scores(f32x16 (&st)[NB], f32x16 (&dpt)[NB], f
 
 template <int D>
 struct BwdCfg {
-  static constexpr int MT = D >= 128 ? 32 : 64;  // moving-tile rows
+  static constexpr int MT = 32;  // moving-tile rows
   static constexpr int NB = MT / 32;
   static constexpr int DS = D / 16, DB = (D + 31) / 32;
   using MTile = Tile<MT, D>;
@@ -398,7 +563,6 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   __syncthreads();
   for (int mt = mt0; mt < nmt; ++mt) {
     const int buf = (mt - mt0) & 1;
-    if (mt + 1 < nmt) fetch(mt + 1, smem + (buf ^ 1) * C::BUF);
     const int m0 = mt * MT;
     bf16* base = smem + buf * C::BUF;
     const bf16* sQ = base;
@@ -447,27 +611,44 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
       }
     }
     __syncthreads();
+    // Transposed dO and Q fragments and this tile's L log2e / D values, all read before the
+    // next tile's direct loads are issued (see fwd_kernel); the loads themselves are issued
+    // by every wave, outside the `active` branches, so no path reaches these reads with a
+    // direct load in flight.
+    bf16x8 ofr[2 * NB][DB], qfr[2 * NB][DB];
+    f32x4 l4[NB][4], d4[NB][4];
+    if (active) {
+#pragma unroll
+      for (int st = 0; st < 2 * NB; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          ofr[st][db] = MTile::tfrag(sdO, 32 * db, 16 * st, lane);
+          qfr[st][db] = MTile::tfrag(sQ, 32 * db, 16 * st, lane);
+        }
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          l4[qb][j] = *reinterpret_cast<const f32x4*>(sL2 + 32 * qb + 8 * j + 4 * g);
+          d4[qb][j] = *reinterpret_cast<const f32x4*>(sD + 32 * qb + 8 * j + 4 * g);
+        }
+    }
+    if (mt + 1 < nmt) fetch(mt + 1, smem + (buf ^ 1) * C::BUF);
     if (active) {
       // Registers: query m0 + 32qb + 8(r/4) + 4g + r%4 against this lane's key; the key is
       // visible iff query >= key, i.e. offset 32qb + 8(r/4) + r%4 >= krow - m0 - 4g.
       if (CAUSAL && m0 < kw0 + 31)
-        dkdv_scores<true, NB>(sp, dp, sL2, sD, c, g, krow - m0 - 4 * g);
+        dkdv_scores<true, NB>(sp, dp, l4, d4, c, krow - m0 - 4 * g);
       else
-        dkdv_scores<false, NB>(sp, dp, sL2, sD, c, g, 0);
+        dkdv_scores<false, NB>(sp, dp, l4, d4, c, 0);
 #pragma unroll
       for (int st = 0; st < 2 * NB; ++st) {
-        bf16x8 ofr[DB], qfr[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          ofr[db] = MTile::tfrag(sdO, 32 * db, 16 * st, lane);
-          qfr[db] = MTile::tfrag(sQ, 32 * db, 16 * st, lane);
-        }
         const bf16x8 pf = to_bf16x8(sp[st >> 1], 8 * (st & 1));
         const bf16x8 sf = to_bf16x8(dp[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvt[db] = mfma32(ofr[db], pf, dvt[db]);
-          dkt[db] = mfma32(qfr[db], sf, dkt[db]);
+          dvt[db] = mfma32(ofr[st][db], pf, dvt[db]);
+          dkt[db] = mfma32(qfr[st][db], sf, dkt[db]);
         }
       }
     }
@@ -528,27 +709,36 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) fetch(kt + 1, smem + (buf ^ 1) * C::BUF);
     const int n0 = kt * MT;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
+    // All LDS reads of this tile before the next tile's direct loads (see fwd_kernel).
+    bf16x8 ka[NB][DS], va[NB][DS], ktf[2 * NB][DB];
     if (active) {
       const bf16* sK = smem + buf * C::BUF;
       const bf16* sV = sK + T;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          ka[kb][s] = MTile::frag(sK, 32 * kb + l32, 2 * s + g);
+          va[kb][s] = MTile::frag(sV, 32 * kb + l32, 2 * s + g);
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2 * NB; ++s2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) ktf[s2][db] = MTile::tfrag(sK, 32 * db, 16 * s2, lane);
+    }
+    if (kt + 1 < nkt) fetch(kt + 1, smem + (buf ^ 1) * C::BUF);
+    if (active) {
       f32x16 st[NB], dpt[NB];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
-        bf16x8 ka[DS], va[DS];
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          ka[s] = MTile::frag(sK, 32 * kb + l32, 2 * s + g);
-          va[s] = MTile::frag(sV, 32 * kb + l32, 2 * s + g);
-        }
         st[kb] = zero16();
         dpt[kb] = zero16();
 #pragma unroll
         for (int s = 0; s < DS; ++s) {
-          st[kb] = mfma32(ka[s], qf[s], st[kb]);
-          dpt[kb] = mfma32(va[s], dof[s], dpt[kb]);
+          st[kb] = mfma32(ka[kb][s], qf[s], st[kb]);
+          dpt[kb] = mfma32(va[kb][s], dof[s], dpt[kb]);
         }
       }
       // Registers: key n0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query.
@@ -559,12 +749,9 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
         dq_scores<false, NB>(st, dpt, c, l2, dsum, 0, 0);
 #pragma unroll
       for (int s2 = 0; s2 < 2 * NB; ++s2) {
-        bf16x8 ktf[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) ktf[db] = MTile::tfrag(sK, 32 * db, 16 * s2, lane);
         const bf16x8 sf = to_bf16x8(dpt[s2 >> 1], 8 * (s2 & 1));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(ktf[db], sf, dqt[db]);
+        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(ktf[s2][db], sf, dqt[db]);
       }
     }
     wait_vmem();
@@ -574,10 +761,9 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
   if (qrow < Nq) store_rows_from_acc<D>(dQh + (size_t)qrow * D, dqt, scale, g);
 }
 
-// One launch for the whole backward. Per head the workgroups run the dK/dV key tiles in
-// order (most visible queries first) and then the dQ query tiles in order (fewest visible
-// keys first), so that the k-th dK/dV tile and the k-th dQ tile, which are dispatched one
-// head-width apart, carry complementary amounts of causal work.
+// One launch for the whole backward. Per head the workgroups run the dK/dV key tiles first
+// and then the dQ query tiles, each kind longest first: the dK/dV tiles that finish first
+// (few visible queries) free their CUs for the longest dQ tiles.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
@@ -603,14 +789,26 @@ __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
     dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, idx * 128, Nq, Nk,
                          scale, neg);
   } else {
-    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, (idx - nkv) * 128, Nq, Nk,
-                       scale, neg);
+    const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
+    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, void* O, float* L,
                  hipStream_t stream) {
+  // Pairing pays off only when one 128-query tile per workgroup leaves CUs idle or runs a
+  // single wave per SIMD anyway; larger grids keep the plain kernel (shared K/V stream, two
+  // waves per SIMD).
+  if constexpr (CAUSAL && D >= 32) {
+    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 128) * s.BH <= kNumCUs) {
+      const long long grid = (long long)(s.Nq / 128) * s.BH;
+      hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
+                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+      return hipGetLastError();
+    }
+  }
   const int nqt = (s.Nq + 127) / 128;
   const long long grid = (long long)nqt * s.BH;
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
