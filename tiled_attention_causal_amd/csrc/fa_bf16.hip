@@ -42,6 +42,26 @@ __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// scale * log2(e) for the exponentials, floored at 1e-30 so that masked scores, set to -inf,
+// give exp2(-inf * c) = 0 even for scale = 0. With c = 1e-30 every visible exponent is below
+// 2^-80 in magnitude, whose exp2 rounds to exactly 1 in fp32: the same P as c = 0.
+__device__ __forceinline__ float exp2_coef(float scale) {
+  return fmaxf(fabsf(scale) * kLog2e, 1e-30f);
+}
+
+// Set score registers whose offset 8(r/4) + r%4 (+32 per block) is not visible to -inf:
+// visible iff lo <= offset <= hi.
+template <int NBLK>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[NBLK], int lo, int hi) {
+#pragma unroll
+  for (int kb = 0; kb < NBLK; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+      if (off < lo || off > hi) s[kb][r] = -INFINITY;
+    }
+}
+
 // Wave index as a scalar, so LDS destinations of the direct loads stay uniform.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -132,24 +152,19 @@ __device__ __forceinline__ void store_rows_from_acc(bf16* out_row,
 }
 
 // Online-softmax update of one 32-query x 64-key score tile held as in fwd_kernel: lane =
-// query, register r of block kb = key offset 32kb + 8(r/4) + 4g + r%4 from the tile start.
-// Rows rescale only when their max grows by more than 2^8 (in exp2 units): until then the
-// stale max keeps every p <= 2^8, and O = acc / l does not depend on which max was used.
-template <bool MASKED, int DB>
+// query, register r of block kb = key offset 32kb + 8(r/4) + 4g + r%4 from the tile start;
+// masked scores are -inf. Rows rescale only when their max grows by more than 2^8 (in exp2
+// units): until then the stale max keeps every p <= 2^8, and O = acc / l does not depend on
+// which max was used.
+template <int DB>
 __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float& l,
-                                             f32x16 (&o)[DB], float c, bool first, int qlim,
-                                             int klim) {
+                                             f32x16 (&o)[DB], float c, bool first) {
   constexpr float kLazy = 8.f;
-  auto vis = [&](int kb, int r) {
-    const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-    return off <= qlim && off < klim;
-  };
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      mx = fmaxf(mx, (!MASKED || vis(kb, r)) ? sacc[kb][r] : -INFINITY);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = fmaxf(mx, swap_halves(mx));
   if (first) {
     m = mx;  // every row sees key 0 in the first tile, so this is finite
@@ -171,8 +186,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float&
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(fmaf(sacc[kb][r], c, nb));
-      if (MASKED && !vis(kb, r)) p = 0.f;
+      const float p = fast_exp2(fmaf(sacc[kb][r], c, nb));
       sacc[kb][r] = p;
       rs += p;
     }
@@ -206,7 +220,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
   const float cs = fabsf(scale);
-  const float c = cs * kLog2e;
+  const float c = exp2_coef(scale);
 
   int nkt = (Nk + BK - 1) / BK;
   if (CAUSAL) nkt = min(nkt, (min(q0 + BQ, Nq) - 1) / BK + 1);
@@ -261,16 +275,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
         for (int s = 0; s < DS; ++s) sacc[kb] = mfma32(kfr[kb][s], qf[s], sacc[kb]);
       }
       // Score registers: key k0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query. Only
-      // tiles that straddle the diagonal or the ragged end of K compare indices; masked
-      // entries are left out of the row max and zeroed after the exponential, which stays
-      // exact for any finite scale (including 0).
-      if ((CAUSAL && k0 + BK - 1 > qw0) || k0 + BK > Nk) {
-        const int qlim = CAUSAL ? qrow - k0 - 4 * g : 1 << 30;  // visible iff offset <= qlim
-        const int klim = Nk - k0 - 4 * g;                       // and offset < klim
-        softmax_tile<true>(sacc, m, l, o, c, kt == 0, qlim, klim);
-      } else {
-        softmax_tile<false>(sacc, m, l, o, c, kt == 0, 0, 0);
-      }
+      // tiles that straddle the diagonal or the ragged end of K compare indices.
+      if ((CAUSAL && k0 + BK - 1 > qw0) || k0 + BK > Nk)
+        mask_scores<2>(sacc, 0, min(CAUSAL ? qrow - k0 - 4 * g : 1 << 30, Nk - 1 - k0 - 4 * g));
+      softmax_tile(sacc, m, l, o, c, kt == 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int pr = w >> 1, wp = w & 1;  // pair, wave within pair
   const float cs = fabsf(scale);
-  const float c = cs * kLog2e;
+  const float c = exp2_coef(scale);
 
   // Steps of this pair: step n works on query tile qt(n) and key tile kt(n).
   //   pair 0: n in [0, s):           A, key tile n
@@ -392,10 +400,8 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 #pragma unroll
         for (int q = 0; q < DS; ++q) sacc[kb] = mfma32(kfr[kb][q], qf[q], sacc[kb]);
       }
-      if (kt == qt)  // the diagonal tile: key offset <= query offset
-        softmax_tile<true>(sacc, m, l, o, c, first, qrow - k0 - 4 * g, 1 << 30);
-      else
-        softmax_tile<false>(sacc, m, l, o, c, first, 0, 0);
+      if (kt == qt) mask_scores<2>(sacc, 0, qrow - k0 - 4 * g);  // the diagonal tile
+      softmax_tile(sacc, m, l, o, c, first);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
@@ -452,61 +458,21 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 }
 
 // ----------------------------------------------------------------------------- backward
-
-// dK/dV pass: P = exp2(S c - L log2e) and dS = P (dP - D) in place, for score registers laid
-// out with lane = key and register r of block qb = query offset 32qb + 8(r/4) + 4g + r%4.
-// Masked (query < key) entries get P = dS = 0.
-template <bool MASKED, int NB>
-__device__ __forceinline__ void dkdv_scores(f32x16 (&sp)[NB], f32x16 (&dp)[NB],
-                                            const f32x4 (&l4)[NB][4], const f32x4 (&d4)[NB][4],
-                                            float c, int lim) {
-#pragma unroll
-  for (int qb = 0; qb < NB; ++qb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * j + i;
-        float p = fast_exp2(fmaf(sp[qb][r], c, -l4[qb][j][i]));
-        if (MASKED && 32 * qb + 8 * j + i < lim) p = 0.f;
-        sp[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - d4[qb][j][i]);
-      }
-}
-
-// dQ pass: the same for lane = query and register r of block kb = key offset
-// 32kb + 8(r/4) + 4g + r%4; visible iff offset <= qlim and offset < klim.
-template <bool MASKED, int NB>
-__device__ __forceinline__ void dq_scores(f32x16 (&st)[NB], f32x16 (&dpt)[NB], float c, float l2,
-                                          float dsum, int qlim, int klim) {
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(fmaf(st[kb][r], c, -l2));
-      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-      if (MASKED && (off > qlim || off >= klim)) p = 0.f;
-      dpt[kb][r] = p * (dpt[kb][r] - dsum);
-    }
-}
+//
+// Both passes step through 32-row moving tiles. A dK/dV step takes 32 queries against the
+// wave's 32 keys (key = lane % 32); a dQ step takes 32 keys against the wave's 32 queries.
 
 template <int D>
-struct BwdCfg {
-  static constexpr int MT = 32;  // moving-tile rows
-  static constexpr int NB = MT / 32;
+struct Bwd {
   static constexpr int DS = D / 16, DB = (D + 31) / 32;
-  using MTile = Tile<MT, D>;
+  using MTile = Tile<32, D>;
   static constexpr int T = MTile::ELEMS;
-  // dK/dV staging: Q, dO, O (row-major), then L (-> L log2e) and D, 64 floats each.
-  static constexpr int BUF_KV = 3 * T + 2 * 64 * 2;
-  // dQ staging: K, V (row-major).
-  static constexpr int BUF_Q = 2 * T;
-  static constexpr int BUF = BUF_KV > BUF_Q ? BUF_KV : BUF_Q;
-  // D = rowsum(dO o O) over the staged tile: CPT 16-byte chunks per thread, TPR threads per
-  // row.
+  // dK/dV stream buffer: Q, dO, O tiles, then 32 floats L (turned into L log2e in place) and
+  // 32 floats D.
+  static constexpr int KV_BUF = 3 * T + 2 * 32 * 2;
+  // dQ stream buffer: K, V tiles.
+  static constexpr int Q_BUF = 2 * T;
   static constexpr int NCH = D / 8;
-  static constexpr int CPT = MT * NCH >= 512 ? 2 : 1;
-  static constexpr int TPR = NCH / CPT;
 };
 
 __device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
@@ -520,26 +486,204 @@ __device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
-// dK, dV for the 128 keys starting at k0 of one head.
+// D = rowsum(dO o O) and L log2e for the 32 staged rows m0.. of a dK/dV stream buffer, by the
+// NTHR threads t = 0 .. NTHR-1 that share the buffer (rows >= Nq get L log2e = +inf, so their
+// P is 0). The caller synchronises before the values are read.
+template <int D, int NTHR>
+__device__ __forceinline__ void kv_stage_rows(bf16* buf, int m0, int Nq, int t) {
+  using B = Bwd<D>;
+  constexpr int CPT = (32 * B::NCH + NTHR - 1) / NTHR;  // chunks per thread
+  constexpr int TPR = B::NCH / CPT;                     // threads per row
+  const bf16* sdO = buf + B::T;
+  const bf16* sO = buf + 2 * B::T;
+  float* sL2 = reinterpret_cast<float*>(buf + 3 * B::T);
+  float* sD = sL2 + 32;
+  const int row = t / TPR, part = t % TPR;
+  float dsum = 0.f;
+  if (row < 32) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = part * CPT + i;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sdO + swz<B::NCH>(row, ch));
+      const u32x4 b = *reinterpret_cast<const u32x4*>(sO + swz<B::NCH>(row, ch));
+      dsum = dot_bf16x8(a, b, dsum);
+    }
+  }
+  dsum = group_sum<TPR>(dsum);
+  if (row < 32 && part == 0) {
+    sD[row] = dsum;
+    sL2[row] = m0 + row < Nq ? sL2[row] * kLog2e : INFINITY;
+  }
+}
+
+// Direct loads of the dK/dV stream for moving tile m0.. (Q, dO, O rows and L) into `buf`,
+// by NW waves (index w).
+template <int D, int NW>
+__device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t Or, rsrc_t Lr, int m0,
+                                         bf16* buf, int w, int lane) {
+  using B = Bwd<D>;
+  B::MTile::template load<NW>(Qr, m0, buf, w, lane);
+  B::MTile::template load<NW>(dOr, m0, buf + B::T, w, lane);
+  B::MTile::template load<NW>(Or, m0, buf + 2 * B::T, w, lane);
+  if (w == 0 && lane < 32) dma4(Lr, (uint32_t)(m0 + lane) * 4, buf + 3 * B::T);
+}
+
+// dK/dV step, first half: S = Q K^T and dP = dO V^T for the 32 staged queries against this
+// wave's 32 keys (kf, vf). Layout: lane = key, register r = query 8(r/4) + 4g + r%4.
+template <int D>
+__device__ __forceinline__ void kv_scores_mfma(const bf16* buf, const bf16x8 (&kf)[D / 16],
+                                               const bf16x8 (&vf)[D / 16], f32x16& sp,
+                                               f32x16& dp, int l32, int g) {
+  using B = Bwd<D>;
+  bf16x8 qa[B::DS], da[B::DS];
+#pragma unroll
+  for (int s = 0; s < B::DS; ++s) {
+    qa[s] = B::MTile::frag(buf, l32, 2 * s + g);
+    da[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
+  }
+  sp = zero16();
+  dp = zero16();
+#pragma unroll
+  for (int s = 0; s < B::DS; ++s) {
+    sp = mfma32(qa[s], kf[s], sp);
+    dp = mfma32(da[s], vf[s], dp);
+  }
+}
+
+// dK/dV step, second half: P = exp2(S c - L log2e), dS = P (dP - D), then dV^T += dO^T P and
+// dK^T += Q^T dS (lane = key, register = column of d). When `masked`, queries with offset
+// 8(r/4) + r%4 below `lim` (earlier than this lane's key) get P = dS = 0. The next tile's
+// direct loads were issued before this step's LDS reads, so the compiler waits for them
+// ahead of the transposed reads below; that latency overlaps the first half of the step.
+template <int D>
+__device__ __forceinline__ void kv_update(const bf16* buf, f32x16& sp, f32x16& dp,
+                                          f32x16 (&dvt)[(D + 31) / 32],
+                                          f32x16 (&dkt)[(D + 31) / 32], float c, bool masked,
+                                          int lim, int lane, int g) {
+  using B = Bwd<D>;
+  constexpr int DB = B::DB;
+  if (masked) {  // queries with offset below lim are earlier than this lane's key
+    f32x16 t[1] = {sp};
+    mask_scores<1>(t, lim, 1 << 30);
+    sp = t[0];
+  }
+  const float* sL2 = reinterpret_cast<const float*>(buf + 3 * B::T);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 8 * j + 4 * g);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sL2 + 32 + 8 * j + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * j + i;
+      const float p = fast_exp2(fmaf(sp[r], c, -l4[i]));
+      sp[r] = p;
+      dp[r] = p * (dp[r] - d4[i]);
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const bf16x8 pf = to_bf16x8(sp, 8 * st);
+    const bf16x8 sf = to_bf16x8(dp, 8 * st);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 dot = B::MTile::tfrag(buf + B::T, 32 * db, 16 * st, lane);
+      const bf16x8 qt = B::MTile::tfrag(buf, 32 * db, 16 * st, lane);
+      dvt[db] = mfma32(dot, pf, dvt[db]);
+      dkt[db] = mfma32(qt, sf, dkt[db]);
+    }
+  }
+}
+
+// dQ step: S^T = K Q^T, dP^T = V dO^T (lane = query, register r = key 8(r/4) + 4g + r%4),
+// P = exp2(S c - L log2e), dS = P (dP - D), dQ^T += K^T dS^T. When `masked`, keys with
+// offset above hi get P = dS = 0.
+template <int D>
+__device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D / 16],
+                                         const bf16x8 (&dof)[D / 16],
+                                         f32x16 (&dqt)[(D + 31) / 32], float c, float l2,
+                                         float dsum, bool masked, int hi, int lane, int l32,
+                                         int g) {
+  using B = Bwd<D>;
+  constexpr int DS = B::DS, DB = B::DB;
+  bf16x8 k[DS], v[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    k[s] = B::MTile::frag(buf, l32, 2 * s + g);
+    v[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
+  }
+  f32x16 st[1] = {zero16()}, dpt = zero16();
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    st[0] = mfma32(k[s], qf[s], st[0]);
+    dpt = mfma32(v[s], dof[s], dpt);
+  }
+  if (masked) mask_scores<1>(st, 0, hi);  // keys with offset above hi are invisible
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = fast_exp2(fmaf(st[0][r], c, -l2));
+    dpt[r] = p * (dpt[r] - dsum);
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const bf16x8 sf = to_bf16x8(dpt, 8 * s2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      dqt[db] = mfma32(B::MTile::tfrag(buf, 32 * db, 16 * s2, lane), sf, dqt[db]);
+  }
+}
+
+// Stationary state of a dQ wave: Q and dO fragments of query row `qrow`, its L log2e and D.
+template <int D>
+struct QRow {
+  bf16x8 qf[D / 16], dof[D / 16];
+  float l2, dsum;
+  __device__ __forceinline__ void load(rsrc_t Qr, rsrc_t dOr, rsrc_t Or, rsrc_t Lr, int qrow,
+                                       int Nq, int g, int neg) {
+    constexpr int DS = D / 16;
+    bf16x8 of[DS];
+    load_frags<D>(qf, Qr, qrow, g);
+    load_frags<D>(dof, dOr, qrow, g);
+    load_frags<D>(of, Or, qrow, g);
+    const float lrow = buf_load_f32(Lr, qrow * 4);
+    wait_vmem();
+    dsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)dof[s][e], (float)of[s][e], dsum);
+    dsum += swap_halves(dsum);
+    l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
+    if (neg)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv_rows(bf16x8 (&kf)[D / 16], bf16x8 (&vf)[D / 16],
+                                             rsrc_t Kr, rsrc_t Vr, int krow, int g, int neg) {
+  load_frags<D>(kf, Kr, krow, g);
+  load_frags<D>(vf, Vr, krow, g);
+  wait_vmem();
+  if (neg)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) kf[s] = negate(kf[s]);
+}
+
+// dK, dV for the 128 keys starting at k0 of one head (4 waves share one query stream).
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
                                           rsrc_t Lr, rsrc_t dOr, bf16* dKh, bf16* dVh, int k0,
                                           int Nq, int Nk, float scale, int neg) {
-  using C = BwdCfg<D>;
-  using MTile = typename C::MTile;
-  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB, T = C::T;
+  using B = Bwd<D>;
+  constexpr int DS = B::DS, DB = B::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int kw0 = k0 + 32 * w;
   const int krow = kw0 + l32;
-  const float c = fabsf(scale) * kLog2e;
+  const float c = exp2_coef(scale);
 
   bf16x8 kf[DS], vf[DS];
-  load_frags<D>(kf, Kr, krow, g);
-  load_frags<D>(vf, Vr, krow, g);
-  if (neg)
-#pragma unroll
-    for (int s = 0; s < DS; ++s) kf[s] = negate(kf[s]);
-
+  load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
   f32x16 dvt[DB], dkt[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -547,111 +691,23 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
     dkt[db] = zero16();
   }
 
-  const int nmt = (Nq + MT - 1) / MT;
-  const int mt0 = CAUSAL ? k0 / MT : 0;
-
-  auto fetch = [&](int mt, bf16* base) {
-    const int m0 = mt * MT;
-    MTile::template load<4>(Qr, m0, base, w, lane);
-    MTile::template load<4>(dOr, m0, base + T, w, lane);
-    MTile::template load<4>(Or, m0, base + 2 * T, w, lane);
-    if (w == 0) dma4(Lr, (uint32_t)(m0 + lane) * 4, base + 3 * T);
-  };
-
-  if (mt0 < nmt) fetch(mt0, smem);
+  const int nmt = (Nq + 31) / 32;
+  const int mt0 = CAUSAL ? k0 / 32 : 0;
+  if (mt0 < nmt) kv_fetch<D, 4>(Qr, dOr, Or, Lr, mt0 * 32, smem, w, lane);
   wait_vmem();
   __syncthreads();
   for (int mt = mt0; mt < nmt; ++mt) {
-    const int buf = (mt - mt0) & 1;
-    const int m0 = mt * MT;
-    bf16* base = smem + buf * C::BUF;
-    const bf16* sQ = base;
-    const bf16* sdO = base + T;
-    const bf16* sO = base + 2 * T;
-    float* sL2 = reinterpret_cast<float*>(base + 3 * T);
-    float* sD = sL2 + 64;
-    const bool active = kw0 < Nk && (!CAUSAL || m0 + MT - 1 >= kw0);
-
-    f32x16 sp[NB], dp[NB];
-    if (active) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        bf16x8 qa[DS], da[DS];
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          qa[s] = MTile::frag(sQ, 32 * qb + l32, 2 * s + g);
-          da[s] = MTile::frag(sdO, 32 * qb + l32, 2 * s + g);
-        }
-        sp[qb] = zero16();
-        dp[qb] = zero16();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          sp[qb] = mfma32(qa[s], kf[s], sp[qb]);
-          dp[qb] = mfma32(da[s], vf[s], dp[qb]);
-        }
-      }
-    }
-    // D and L log2e for the tile's rows, while the MFMAs above run.
-    {
-      const int row = tid / C::TPR, part = tid % C::TPR;
-      float dsum = 0.f;
-      if (row < MT) {
-#pragma unroll
-        for (int i = 0; i < C::CPT; ++i) {
-          const int ch = part * C::CPT + i;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sdO + swz<C::NCH>(row, ch));
-          const u32x4 b = *reinterpret_cast<const u32x4*>(sO + swz<C::NCH>(row, ch));
-          dsum = dot_bf16x8(a, b, dsum);
-        }
-      }
-      dsum = group_sum<C::TPR>(dsum);
-      if (row < MT && part == 0) {
-        sD[row] = dsum;
-        sL2[row] = m0 + row < Nq ? sL2[row] * kLog2e : INFINITY;
-      }
-    }
+    bf16* buf = smem + ((mt - mt0) & 1) * B::KV_BUF;
+    bf16* nbuf = smem + (((mt - mt0) & 1) ^ 1) * B::KV_BUF;
+    const int m0 = mt * 32;
+    const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
+    if (mt + 1 < nmt) kv_fetch<D, 4>(Qr, dOr, Or, Lr, m0 + 32, nbuf, w, lane);
+    f32x16 sp, dp;
+    if (active) kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
+    kv_stage_rows<D, 256>(buf, m0, Nq, tid);
     __syncthreads();
-    // Transposed dO and Q fragments and this tile's L log2e / D values, all read before the
-    // next tile's direct loads are issued (see fwd_kernel); the loads themselves are issued
-    // by every wave, outside the `active` branches, so no path reaches these reads with a
-    // direct load in flight.
-    bf16x8 ofr[2 * NB][DB], qfr[2 * NB][DB];
-    f32x4 l4[NB][4], d4[NB][4];
-    if (active) {
-#pragma unroll
-      for (int st = 0; st < 2 * NB; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          ofr[st][db] = MTile::tfrag(sdO, 32 * db, 16 * st, lane);
-          qfr[st][db] = MTile::tfrag(sQ, 32 * db, 16 * st, lane);
-        }
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          l4[qb][j] = *reinterpret_cast<const f32x4*>(sL2 + 32 * qb + 8 * j + 4 * g);
-          d4[qb][j] = *reinterpret_cast<const f32x4*>(sD + 32 * qb + 8 * j + 4 * g);
-        }
-    }
-    if (mt + 1 < nmt) fetch(mt + 1, smem + (buf ^ 1) * C::BUF);
-    if (active) {
-      // Registers: query m0 + 32qb + 8(r/4) + 4g + r%4 against this lane's key; the key is
-      // visible iff query >= key, i.e. offset 32qb + 8(r/4) + r%4 >= krow - m0 - 4g.
-      if (CAUSAL && m0 < kw0 + 31)
-        dkdv_scores<true, NB>(sp, dp, l4, d4, c, krow - m0 - 4 * g);
-      else
-        dkdv_scores<false, NB>(sp, dp, l4, d4, c, 0);
-#pragma unroll
-      for (int st = 0; st < 2 * NB; ++st) {
-        const bf16x8 pf = to_bf16x8(sp[st >> 1], 8 * (st & 1));
-        const bf16x8 sf = to_bf16x8(dp[st >> 1], 8 * (st & 1));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dvt[db] = mfma32(ofr[st][db], pf, dvt[db]);
-          dkt[db] = mfma32(qfr[st][db], sf, dkt[db]);
-        }
-      }
-    }
+    if (active)
+      kv_update<D>(buf, sp, dp, dvt, dkt, c, CAUSAL && m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
     wait_vmem();
     __syncthreads();
   }
@@ -662,98 +718,45 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   }
 }
 
-// dQ for the 128 queries starting at q0 of one head.
+// dQ for the 128 queries starting at q0 of one head (4 waves share one key stream).
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
                                         rsrc_t Lr, rsrc_t dOr, bf16* dQh, int q0, int Nq, int Nk,
                                         float scale, int neg) {
-  using C = BwdCfg<D>;
-  using MTile = typename C::MTile;
-  constexpr int MT = C::MT, NB = C::NB, DS = C::DS, DB = C::DB, T = C::T;
+  using B = Bwd<D>;
+  constexpr int DB = B::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int qw0 = q0 + 32 * w;
   const int qrow = qw0 + l32;
-  const float c = fabsf(scale) * kLog2e;
+  const float c = exp2_coef(scale);
 
-  bf16x8 qf[DS], dof[DS], of[DS];
-  load_frags<D>(qf, Qr, qrow, g);
-  load_frags<D>(dof, dOr, qrow, g);
-  load_frags<D>(of, Or, qrow, g);
-  const float lrow = buf_load_f32(Lr, qrow * 4);
-  wait_vmem();
-  float dsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < DS; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dsum = fmaf((float)dof[s][e], (float)of[s][e], dsum);
-  dsum += swap_halves(dsum);
-  const float l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
-  if (neg)
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
-
+  QRow<D> row;
+  row.load(Qr, dOr, Or, Lr, qrow, Nq, g, neg);
   f32x16 dqt[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqt[db] = zero16();
 
-  int nkt = (Nk + MT - 1) / MT;
-  if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / MT + 1);
-
-  auto fetch = [&](int kt, bf16* base) {
-    MTile::template load<4>(Kr, kt * MT, base, w, lane);
-    MTile::template load<4>(Vr, kt * MT, base + T, w, lane);
-  };
-
-  if (nkt > 0) fetch(0, smem);
+  int nkt = (Nk + 31) / 32;
+  if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / 32 + 1);
+  if (nkt > 0) {
+    B::MTile::template load<4>(Kr, 0, smem, w, lane);
+    B::MTile::template load<4>(Vr, 0, smem + B::T, w, lane);
+  }
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const int n0 = kt * MT;
+    const bf16* buf = smem + (kt & 1) * B::Q_BUF;
+    bf16* nbuf = smem + ((kt & 1) ^ 1) * B::Q_BUF;
+    const int n0 = kt * 32;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
-    // All LDS reads of this tile before the next tile's direct loads (see fwd_kernel).
-    bf16x8 ka[NB][DS], va[NB][DS], ktf[2 * NB][DB];
-    if (active) {
-      const bf16* sK = smem + buf * C::BUF;
-      const bf16* sV = sK + T;
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          ka[kb][s] = MTile::frag(sK, 32 * kb + l32, 2 * s + g);
-          va[kb][s] = MTile::frag(sV, 32 * kb + l32, 2 * s + g);
-        }
-#pragma unroll
-      for (int s2 = 0; s2 < 2 * NB; ++s2)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) ktf[s2][db] = MTile::tfrag(sK, 32 * db, 16 * s2, lane);
+    if (kt + 1 < nkt) {
+      B::MTile::template load<4>(Kr, n0 + 32, nbuf, w, lane);
+      B::MTile::template load<4>(Vr, n0 + 32, nbuf + B::T, w, lane);
     }
-    if (kt + 1 < nkt) fetch(kt + 1, smem + (buf ^ 1) * C::BUF);
-    if (active) {
-      f32x16 st[NB], dpt[NB];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        st[kb] = zero16();
-        dpt[kb] = zero16();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          st[kb] = mfma32(ka[kb][s], qf[s], st[kb]);
-          dpt[kb] = mfma32(va[kb][s], dof[s], dpt[kb]);
-        }
-      }
-      // Registers: key n0 + 32kb + 8(r/4) + 4g + r%4 against this lane's query.
-      if ((CAUSAL && n0 + MT - 1 > qw0) || n0 + MT > Nk)
-        dq_scores<true, NB>(st, dpt, c, l2, dsum, CAUSAL ? qrow - n0 - 4 * g : 1 << 30,
-                            Nk - n0 - 4 * g);
-      else
-        dq_scores<false, NB>(st, dpt, c, l2, dsum, 0, 0);
-#pragma unroll
-      for (int s2 = 0; s2 < 2 * NB; ++s2) {
-        const bf16x8 sf = to_bf16x8(dpt[s2 >> 1], 8 * (s2 & 1));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) dqt[db] = mfma32(ktf[s2][db], sf, dqt[db]);
-      }
-    }
+    if (active)
+      q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.dsum,
+                  (CAUSAL && n0 + 31 > qw0) || n0 + 32 > Nk,
+                  min(CAUSAL ? qrow - n0 - 4 * g : 1 << 30, Nk - 1 - n0 - 4 * g), lane, l32, g);
     wait_vmem();
     __syncthreads();
   }
@@ -765,7 +768,7 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
 // and then the dQ query tiles, each kind longest first: the dK/dV tiles that finish first
 // (few visible queries) free their CUs for the longest dQ tiles.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
                                                   const bf16* __restrict__ V,
                                                   const bf16* __restrict__ O,
@@ -774,7 +777,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
                                                   bf16* __restrict__ dQ, bf16* __restrict__ dK,
                                                   bf16* __restrict__ dV, int Nq, int Nk,
                                                   float scale, int neg) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * BwdCfg<D>::BUF];
+  constexpr int SM = Bwd<D>::KV_BUF > Bwd<D>::Q_BUF ? Bwd<D>::KV_BUF : Bwd<D>::Q_BUF;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * SM];
   const int nkv = (Nk + 127) / 128, nqw = (Nq + 127) / 128;
   const int per_head = nkv + nqw;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -791,6 +795,187 @@ __global__ __launch_bounds__(256) void bwd_kernel(const bf16* __restrict__ Q,
   } else {
     const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
     dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
+  }
+}
+
+// Causal backward with complementary tile pairing, for Nq = Nk = N, N % 128 == 0 (the
+// counterpart of fwd_causal_paired_kernel). Tiles are 64 rows, held by a wave pair (32 rows
+// per wave); steps are 32-row moving tiles. Per head, T/2 workgroups do dK/dV and T/2 do dQ
+// (T = N/64):
+//   dK/dV workgroup j: key tile A = j sees query steps 2j .. 2T-1 (2(T-j) steps) and key tile
+//     B = T-1-j sees 2(j+1) steps: 2(T+1) together. Pair 0 runs A's first T+1 steps; pair 1
+//     runs B and then A's remaining T-2j-1 steps.
+//   dQ workgroup i: query tile A = T-1-i sees key steps 0 .. 2(T-i)-1 and B = i sees
+//     2(i+1): pair 0 runs A's first T+1 steps, pair 1 runs B and then A's rest.
+// Both pairs make exactly T+1 steps in lockstep, each with its own stream; pair 1 then adds its
+// partial sums for A into pair 0's through LDS.
+template <int D>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ O, const float* __restrict__ L, const bf16* __restrict__ dO,
+    bf16* __restrict__ dQ, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale,
+    int neg) {
+  using B = Bwd<D>;
+  constexpr int DS = B::DS, DB = B::DB;
+  constexpr int SM = B::KV_BUF > B::Q_BUF ? B::KV_BUF : B::Q_BUF;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2][2][SM];  // [pair][buffer]
+
+  const int T = N / 64, half = T / 2;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / T, idx = lid % T;
+  const size_t o = (size_t)bh * N * D;
+  const uint32_t nb = (uint32_t)N * D * 2;
+  const rsrc_t Qr = make_rsrc(Q + o, nb), Or = make_rsrc(O + o, nb), dOr = make_rsrc(dO + o, nb);
+  const rsrc_t Kr = make_rsrc(K + o, nb), Vr = make_rsrc(V + o, nb);
+  const rsrc_t Lr = make_rsrc(L + (size_t)bh * N, (uint32_t)N * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int pr = w >> 1, wp = w & 1, pt = tid & 127;  // pair, wave in pair, thread in pair
+  const float c = exp2_coef(scale);
+  const int nsteps = T + 1;
+  constexpr int XS = 2 * 16 * DB;  // merge record per lane: up to two accumulator sets
+
+  if (idx < half) {
+    // ---------------------------------------------------------------- dK / dV workgroup
+    const int tA = idx, tB = T - 1 - idx;
+    const int nB = 2 * (tB == tA ? 0 : idx + 1);  // steps of B (pair 1), 2(j+1)
+    // step n of this pair -> key tile and moving query tile
+    auto kt_of = [&](int n) { return (pr == 0 || n >= nB) ? tA : tB; };
+    auto mt_of = [&](int n) {
+      return pr == 0 ? 2 * tA + n : (n < nB ? 2 * tB + n : 2 * tA + nsteps + (n - nB));
+    };
+    int kt = kt_of(0);
+    int krow = 64 * kt + 32 * wp + l32;
+    bf16x8 kf[DS], vf[DS];
+    load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
+    f32x16 dvt[DB], dkt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dvt[db] = zero16();
+      dkt[db] = zero16();
+    }
+    kv_fetch<D, 2>(Qr, dOr, Or, Lr, 32 * mt_of(0), smem[pr][0], wp, lane);
+    wait_vmem();
+    __syncthreads();
+    for (int n = 0; n < nsteps; ++n) {
+      bf16* buf = smem[pr][n & 1];
+      bf16* nbuf = smem[pr][(n & 1) ^ 1];
+      const int m0 = 32 * mt_of(n);
+      const int kw0 = 64 * kt + 32 * wp;
+      const bool active = m0 + 31 >= kw0;
+      if (n + 1 < nsteps) kv_fetch<D, 2>(Qr, dOr, Or, Lr, 32 * mt_of(n + 1), nbuf, wp, lane);
+      f32x16 sp, dp;
+      if (active) kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
+      kv_stage_rows<D, 128>(buf, m0, N, pt);
+      __syncthreads();
+      if (active)
+        kv_update<D>(buf, sp, dp, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
+      if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
+        store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
+        store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvt[db] = zero16();
+          dkt[db] = zero16();
+        }
+        kt = tA;
+        krow = 64 * kt + 32 * wp + l32;
+        load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+    // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end).
+    const bool p1_has_A = nsteps > nB;
+    float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
+    static_assert(2 * 64 * XS * sizeof(float) <= sizeof(smem), "merge area must fit");
+    if (pr == 1 && p1_has_A) {
+      float* x = xf + (wp * 64 + lane) * XS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          x[16 * db + r] = dkt[db][r];
+          x[16 * (DB + db) + r] = dvt[db][r];
+        }
+    }
+    __syncthreads();
+    if (pr == 0) {
+      if (p1_has_A) {
+        const float* x = xf + (wp * 64 + lane) * XS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dkt[db][r] += x[16 * db + r];
+            dvt[db][r] += x[16 * (DB + db) + r];
+          }
+      }
+      store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
+      store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+    }
+  } else {
+    // ------------------------------------------------------------------------ dQ workgroup
+    const int i = idx - half;
+    const int tA = T - 1 - i, tB = i;
+    const int nB = 2 * (i + 1);
+    auto qt_of = [&](int n) { return (pr == 0 || n >= nB) ? tA : tB; };
+    auto kt_of = [&](int n) { return pr == 0 ? n : (n < nB ? n : nsteps + (n - nB)); };
+    int qt = qt_of(0);
+    int qrow = 64 * qt + 32 * wp + l32;
+    QRow<D> row;
+    row.load(Qr, dOr, Or, Lr, qrow, N, g, neg);
+    f32x16 dqt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqt[db] = zero16();
+    B::MTile::template load<2>(Kr, 32 * kt_of(0), smem[pr][0], wp, lane);
+    B::MTile::template load<2>(Vr, 32 * kt_of(0), smem[pr][0] + B::T, wp, lane);
+    wait_vmem();
+    __syncthreads();
+    for (int n = 0; n < nsteps; ++n) {
+      const bf16* buf = smem[pr][n & 1];
+      bf16* nbuf = smem[pr][(n & 1) ^ 1];
+      const int n0 = 32 * kt_of(n);
+      const int qw0 = 64 * qt + 32 * wp;
+      const bool active = n0 <= qw0 + 31;
+      if (n + 1 < nsteps) {
+        B::MTile::template load<2>(Kr, 32 * kt_of(n + 1), nbuf, wp, lane);
+        B::MTile::template load<2>(Vr, 32 * kt_of(n + 1), nbuf + B::T, wp, lane);
+      }
+      if (active)
+        q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.dsum, n0 + 31 > qw0,
+                    qrow - n0 - 4 * g, lane, l32, g);
+      if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
+        store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dqt[db] = zero16();
+        qt = tA;
+        qrow = 64 * qt + 32 * wp + l32;
+        row.load(Qr, dOr, Or, Lr, qrow, N, g, neg);
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+    const bool p1_has_A = nsteps > nB;
+    float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
+    if (pr == 1 && p1_has_A) {
+      float* x = xf + (wp * 64 + lane) * XS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[16 * db + r] = dqt[db][r];
+    }
+    __syncthreads();
+    if (pr == 0) {
+      if (p1_has_A) {
+        const float* x = xf + (wp * 64 + lane) * XS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dqt[db][r] += x[16 * db + r];
+      }
+      store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
+    }
   }
 }
 
@@ -821,6 +1006,20 @@ template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* O,
                  const float* L, const void* dO, void* dQ, void* dK, void* dV,
                  hipStream_t stream) {
+  // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
+  // the longest tile on the critical path of a small grid; see bwd_causal_paired_kernel.
+  // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
+  // instantiation, so it is not built.)
+  if constexpr (CAUSAL && D >= 32 && D <= 64) {
+    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 2 * kNumCUs) {
+      const long long grid = (long long)(s.Nq / 64) * s.BH;
+      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
+                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)O,
+                         L, (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
+                         s.scale < 0.f ? 1 : 0);
+      return hipGetLastError();
+    }
+  }
   const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH;
   hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)O, L,
