@@ -217,3 +217,56 @@ def test_autograd_function(gpu):
     dq, dk, dv = fa_backward(q, k, v, o2, lse, do, True)
     assert torch.equal(o, o2)
     assert torch.equal(qr.grad, dq) and torch.equal(kr.grad, dk) and torch.equal(vr.grad, dv)
+
+
+# Causal square shapes small enough (B*H*N/128 <= 256 CUs for the forward, B*H*N/64 <= 512
+# for the backward) to take the paired kernels, whose pair 1 switches tiles part-way and
+# whose partial sums meet in LDS; T = N/64 covers the smallest grid (T = 2, pair 1 without a
+# share of the long tile) and odd and even numbers of tile pairs.
+PAIRED = [
+    (1, 1, 128, 64),
+    (1, 2, 256, 64),
+    (2, 1, 384, 32),
+    (1, 1, 640, 64),
+    (1, 3, 512, 32),
+    (1, 1, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("case", PAIRED, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_paired_causal_kernels_match_oracle(gpu, case):
+    B, H, N, d = case
+    note(f"paired case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=8400 + N + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    compare(got, full_oracle(inp, True, scale), "bf16")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_paired_causal_kernels_unusual_scale(gpu, scale):
+    inp = make_inputs(1, 2, 384, 384, 64, "bf16", index=8500)
+    got = run_gpu(inp, True, scale, gpu)
+    ref = full_oracle(inp, True, scale)
+    for h in range(2):
+        a = [to_f64(inp[n][0, h]) for n in ("q", "k", "v", "do")]
+        allow = o_rounding_allowance(*a, True, scale)
+        for n in ("O", "L", "dQ", "dK", "dV"):
+            check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
+
+
+def test_paired_and_plain_forward_agree(gpu):
+    """The same inputs through the paired and plain kernels: the grid-size switch only
+    changes the order of the key-tile sums, so O and L agree to fp32 rounding."""
+    from tiled_attention_causal_amd import fa_forward
+    inp = make_inputs(1, 1, 512, 512, 64, "bf16", index=8600)
+    q, k, v = (inp[n].to(gpu) for n in ("q", "k", "v"))
+    o1, l1 = fa_forward(q, k, v, True, 0.125)               # 4 tiles: paired
+    rep = 80                                                 # 80 * 4 tiles > 256: plain
+    o2, l2 = fa_forward(q.repeat(1, rep, 1, 1), k.repeat(1, rep, 1, 1),
+                        v.repeat(1, rep, 1, 1), True, 0.125)
+    torch.cuda.synchronize(gpu)
+    for h in (0, rep - 1):
+        assert torch.allclose(l1[0, 0], l2[0, h], atol=1e-5, rtol=0)
+        a, b = o1[0, 0].float(), o2[0, h].float()
+        assert torch.all((a - b).abs() <= 2 ** -7 * a.abs().clamp(min=1.0))

@@ -88,14 +88,13 @@ struct Tile {
   // the global chunk whose swizzled position is p; rows past the head's end read as zeros.
   template <int NW>
   __device__ __forceinline__ static void load(rsrc_t src, int row0, bf16* t, int w, int lane) {
-    constexpr int M = NCH < 8 ? NCH - 1 : 7;
 #pragma unroll
     for (int i = 0; i < (NKIB + NW - 1) / NW; ++i) {
       const int blk = w + i * NW;
       if (NKIB % NW == 0 || blk < NKIB) {
         const int p = blk * 64 + lane;
         const int row = p / NCH, cp = p % NCH;
-        const int gc = cp ^ ((row ^ (row >> 3)) & M);
+        const int gc = cp ^ swz_key<NCH>(row);
         dma16(src, (uint32_t)(((row0 + row) * C + gc * 8) * 2), t + blk * 512);
       }
     }
@@ -153,9 +152,9 @@ __device__ __forceinline__ void store_rows_from_acc(bf16* out_row,
 
 // Online-softmax update of one 32-query x 64-key score tile held as in fwd_kernel: lane =
 // query, register r of block kb = key offset 32kb + 8(r/4) + 4g + r%4 from the tile start;
-// masked scores are -inf. Rows rescale only when their max grows by more than 2^8 (in exp2
-// units): until then the stale max keeps every p <= 2^8, and O = acc / l does not depend on
-// which max was used.
+// masked scores are -inf. Leaves p in sacc (the row sum is taken by p_operands). Rows rescale
+// only when their max grows by more than 2^8 (in exp2 units): until then the stale max keeps
+// every p <= 2^8, and O = acc / l does not depend on which max was used.
 template <int DB>
 __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float& l,
                                              f32x16 (&o)[DB], float c, bool first) {
@@ -181,15 +180,22 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float&
     }
   }
   const float nb = -m * c;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, nb));
+}
+
+// P as the four bf16 operands of the P V product, and its fp32 row sum (L = m + log l must
+// not pass through bf16).
+__device__ __forceinline__ void p_operands(const f32x16 (&sacc)[2], bf16x8 (&pf)[4], float& l) {
   float rs = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(sacc[kb][r], c, nb));
-      sacc[kb][r] = p;
-      rs += p;
-    }
+    for (int r = 0; r < 16; ++r) rs += sacc[kb][r];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pf[u] = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
   l += rs;
 }
 
@@ -279,12 +285,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
       if ((CAUSAL && k0 + BK - 1 > qw0) || k0 + BK > Nk)
         mask_scores<2>(sacc, 0, min(CAUSAL ? qrow - k0 - 4 * g : 1 << 30, Nk - 1 - k0 - 4 * g));
       softmax_tile(sacc, m, l, o, c, kt == 0);
+      bf16x8 pf[4];
+      p_operands(sacc, pf, l);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf, o[db]);
-      }
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf[u], o[db]);
     }
     wait_vmem();
     __syncthreads();
@@ -402,12 +408,12 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
       }
       if (kt == qt) mask_scores<2>(sacc, 0, qrow - k0 - 4 * g);  // the diagonal tile
       softmax_tile(sacc, m, l, o, c, first);
+      bf16x8 pf[4];
+      p_operands(sacc, pf, l);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 pf = to_bf16x8(sacc[u >> 1], 8 * (u & 1));
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf, o[db]);
-      }
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf[u], o[db]);
       if (pr == 1 && n == tB) finish_B();
     }
     wait_vmem();
@@ -477,12 +483,7 @@ struct Bwd {
 
 __device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = fmaf(__builtin_bit_cast(float, a[i] << 16), __builtin_bit_cast(float, b[i] << 16),
-               acc);
-    acc = fmaf(__builtin_bit_cast(float, a[i] & 0xFFFF0000u),
-               __builtin_bit_cast(float, b[i] & 0xFFFF0000u), acc);
-  }
+  for (int i = 0; i < 4; ++i) acc = dot2_bf16(a[i], b[i], acc);
   return acc;
 }
 
@@ -649,8 +650,8 @@ struct QRow {
     dsum = 0.f;
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsum = fmaf((float)dof[s][e], (float)of[s][e], dsum);
+      dsum = dot_bf16x8(__builtin_bit_cast(u32x4, dof[s]), __builtin_bit_cast(u32x4, of[s]),
+                        dsum);
     dsum += swap_halves(dsum);
     l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
     if (neg)

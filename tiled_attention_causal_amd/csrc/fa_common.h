@@ -34,6 +34,13 @@ __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// v_dot2c_f32_bf16: acc + a.x * b.x + a.y * b.y for two bf16 pairs packed in 32 bits.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
 // Wait until every outstanding vector-memory load of this wave has returned.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -80,13 +87,24 @@ __device__ __forceinline__ int chunk_row(int kc, int e) {
   return 16 * (kc >> 1) + 8 * (e >> 2) + 4 * (kc & 1) + (e & 3);
 }
 
+// XOR key of row r for an LDS tile with NCH 16-byte chunks per row. With 8 or more chunks
+// the key is 2(r%4) ^ ((r/4)%2): eight consecutive rows reading one chunk (an MFMA row
+// fragment) get eight distinct keys, and four consecutive rows reading a pair of adjacent
+// chunks (a transposed fragment, ds_read_b64_tr_b16) get four disjoint chunk pairs, so
+// neither pattern repeats an LDS bank. Narrower tiles use (r ^ r/8) % NCH.
+template <int NCH>
+__device__ __forceinline__ int swz_key(int r) {
+  if constexpr (NCH >= 8)
+    return ((r & 3) << 1) ^ ((r >> 2) & 1);
+  else
+    return (r ^ (r >> 3)) & (NCH - 1);
+}
+
 // Element offset of 16-byte chunk c of row r in an LDS tile with NCH chunks per row and no
-// padding. Chunks are XOR-swizzled by (r ^ r>>3) so that eight consecutive rows reading the
-// same chunk, and rows 8 apart writing the same chunk, fall in different bank groups.
+// padding; chunk c of row r is stored at position c ^ swz_key(r).
 template <int NCH>
 __device__ __forceinline__ int swz(int r, int c) {
-  constexpr int M = NCH < 8 ? NCH - 1 : 7;
-  return r * (NCH * 8) + ((c ^ ((r ^ (r >> 3)) & M)) << 3);
+  return r * (NCH * 8) + ((c ^ swz_key<NCH>(r)) << 3);
 }
 
 template <int NCH>
