@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="stop the oracle sample after this much CPU work")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="run the oracle sample for at least this much CPU time")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all", action="store_true")
     return ap.parse_args()
@@ -52,10 +52,29 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per backward launch from the committed rocprofv3 counter summary, or None
+def kernel_names(w):
+    """Names of the forward and backward kernels the library launches for workload `w`
+    following the dispatch rules of fa_bf16.hip and fa_f32.hip: the paired causal kernels
+    serve square causal grids of 128-row tiles that fit the chip in one wave of workgroups
+    (the backward pairing is built for d = 32 and 64 only)."""
+    c = "true" if w.causal else "false"
+    if w.dtype == "f32":
+        return f"fwd_f32_kernel<{w.d}, {c}>", f"dkdv_f32_kernel+dq_f32_kernel<{w.d}, {c}>"
+    n_cus = 256
+    square = w.causal and w.Nq == w.Nk and w.Nq % 128 == 0 and w.d >= 32
+    fwd = (f"fwd_causal_paired_kernel<{w.d}>"
+           if square and (w.Nq // 128) * w.B * w.H <= n_cus else f"fwd_kernel<{w.d}, {c}>")
+    bwd = (f"bwd_causal_paired_kernel<{w.d}>"
+           if square and w.d <= 64 and (w.Nq // 64) * w.B * w.H <= 2 * n_cus
+           else f"bwd_kernel<{w.d}, {c}>")
+    return fwd, bwd
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
     when the summary is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"bwd_kernel_{workload}_traffic.txt")
+    stem = kernel.split("<")[0]
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -121,8 +140,8 @@ def time_workload(w, steps, warmup):
     }
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle on whole heads of the same workload until `budget_s` is spent."""
+def cpu_baseline(w, min_s, budget_s):
+    """The fp64 oracle on whole heads of the same workload for about `min_s` seconds."""
     import numpy as np
 
     import oracle
@@ -136,20 +155,25 @@ def cpu_baseline(w, budget_s):
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = 0
     t0 = time.perf_counter()
-    for b, h in heads:
+    # Whole heads in order, wrapping round, until at least `min_s` and at most `budget_s`
+    # seconds of oracle work are done (a head is never cut short).
+    while True:
+        b, h = heads[done % len(heads)]
         a = [to_f64(inp[n][b, h]) for n in ("q", "k", "v", "do")]
         oracle.head_forward(a[0], a[1], a[2], w.causal, w.scale)
         oracle.head_backward(a[0], a[1], a[2], a[3], w.causal, w.scale)
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
+        el = time.perf_counter() - t0
+        per_head = el / done
+        if el >= min_s or el + per_head > budget_s:
             break
-    el = time.perf_counter() - t0
     flops = w.counted_flops()["total"] * done / len(heads)
     del np
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads (one head: B=1,H=1,N={w.Nq},d={w.d}), "
-                      f"fp64 forward + backward, {el:.1f} s; counted FLOPs as on the GPU"}
+            "sample": f"{done} head passes over the {len(heads)} heads of the workload (one "
+                      f"head: B=1,H=1,N={w.Nq},d={w.d}), fp64 forward + backward, {el:.1f} s; "
+                      f"counted FLOPs as on the GPU"}
 
 
 def copy_calibration():
@@ -200,9 +224,10 @@ def main():
                   f"  step {rr['ms_per_step']:.4f} ms "
                   f"({f2['total'] / rr['ms_per_step'] / 1e9:.1f} TF/s)", file=sys.stderr)
 
+    fwd_name, bwd_name = kernel_names(w)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, 3.0 * args.cpu_seconds)
 
     out = {
         "metric": "causal attention fwd+bwd TFLOP/s (bf16, d=64) and % of MFMA peak",
@@ -220,12 +245,13 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype},
-        "passes": {"fwd_ms": round(r["fwd_ms_mean"], 5), "fwd_tflops": round(fwd_tf, 2),
+        "passes": {"fwd_kernel": fwd_name, "fwd_ms": round(r["fwd_ms_mean"], 5),
+                   "fwd_tflops": round(fwd_tf, 2), "bwd_kernel": bwd_name,
                    "bwd_ms": round(r["bwd_ms_mean"], 5), "bwd_tflops": round(bwd_tf, 2)},
-        "roofline": {"kernel": "bwd_kernel", "bound": "mfma", "achieved": round(bwd_tf, 2),
+        "roofline": {"kernel": bwd_name, "bound": "mfma", "achieved": round(bwd_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": read_traffic(w.name)},
+                     "traffic": read_traffic(w.name, bwd_name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
