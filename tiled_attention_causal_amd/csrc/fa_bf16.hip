@@ -164,7 +164,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[2], float& m, float&
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = halves_max(mx);
   if (first) {
     m = mx;  // every row sees key 0 in the first tile, so this is finite
   } else {
@@ -268,6 +268,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
       KTile::template load<4>(Vr, (kt + 1) * BK, nb + KTile::ELEMS, w, lane);
     }
     if (active) {
+      // K fragments are read where they are used: requesting them up front with V's would
+      // cost registers, and this kernel relies on two or three waves per SIMD.
       bf16x8 kfr[2][DS];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
     __syncthreads();
   }
 
-  const float lt = l + swap_halves(l);
+  const float lt = halves_sum(l);
   if (qrow < Nq) {
     store_rows_from_acc<D>(O + ((size_t)bh * Nq + qrow) * D, o, 1.f / lt, g);
     if (g == 0) Lout[(size_t)bh * Nq + qrow] = m * cs + logf(lt);
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
     KTile::template load<2>(Vr, k0, dst[1], wp, lane);
   };
   auto finish_B = [&]() {  // pair 1, after B's last key tile: B is complete
-    const float lt = l + swap_halves(l);
+    const float lt = halves_sum(l);
     const int row = 64 * tB + 32 * wp + l32;
     store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
     if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
@@ -381,24 +383,27 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   auto step = [&](int n, const bf16 (*cur)[KT], bf16 (*nxt)[KT]) {
     // The transposed V reads come before the next tile's direct loads: the compiler cannot
     // tell that they do not alias and would otherwise wait for those loads to land first.
-    bf16x8 vfr[4][DB];
-    if (n < nsteps)
+    // All of this step's LDS operands are requested up front, so the score MFMAs wait for the
+    // first K fragment only (this kernel runs one wave per SIMD, so registers are plentiful).
+    bf16x8 vfr[4][DB], kfr[2][DS];
+    if (n < nsteps) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(cur[1], 32 * db, 16 * u, lane);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(cur[0], 32 * kb + l32, 2 * q + g);
+    }
     if (n + 1 < nsteps) fetch(n + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
     if (n < nsteps) {
       const int qt = qt_of(n), kt = kt_of(n);
       const bool first = pr == 0 ? n == 0 : (n == 0 || n == tB + 1);
       const int qrow = 64 * qt + 32 * wp + l32;
       const int k0 = kt * BK;
       const bf16x8(&qf)[DS] = qt == tA ? qfA : qfB;
-      bf16x8 kfr[2][DS];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(cur[0], 32 * kb + l32, 2 * q + g);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -456,11 +461,181 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
       l = l * a0 + l1 * a1;
       m = mm;
     }
-    const float lt = l + swap_halves(l);
+    const float lt = halves_sum(l);
     const int row = 64 * tA + 32 * wp + l32;
     store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
     if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
   }
+}
+
+// Causal forward for Nq = Nk = N, N % 128 == 0, 32 <= d <= 64, on eight waves (two per SIMD).
+//
+// As in fwd_causal_paired_kernel, workgroup i takes the 64-row query tiles A = T-1-i and
+// B = i (T = N/64), which need T + 1 key steps together: A over key tiles 0 .. T-i-1, then
+// B over key tiles 0 .. i. Here that sequence is cut into NP = 4 contiguous runs of equal
+// length (within one), one per wave pair, and the pairs step in lockstep with their own K/V
+// streams. A run that crosses from A into B parks its partial (m, l, O) for A in LDS and
+// starts B afresh. At the end every pair parks its last partial; pair 0 merges those of A
+// and pair NP-1 those of B, with the rescale the online softmax uses between key tiles, and
+// stores O and L.
+template <int D>
+__global__ __launch_bounds__(512) void fwd_causal_split_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg) {
+  constexpr int NP = 4, BK = 64;
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
+  using KTile = Tile<BK, D>;
+  constexpr int KT = KTile::ELEMS;
+  constexpr int XS = 16 * DB + 2;  // parked partial: O registers, m, l (component-major)
+  __shared__ __attribute__((aligned(1024))) bf16 kv[NP][2][2][KT];  // [pair][buffer][K | V]
+  __shared__ __attribute__((aligned(16))) float park_cross[XS * 128];
+  static_assert(NP * XS * 128 * sizeof(float) <= sizeof(kv), "parked partials must fit in kv");
+
+  const int T = N / 64, half = T / 2;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / half, i = lid % half;
+  const int tA = T - 1 - i, tB = i, nA = T - i, S = T + 1;
+  const rsrc_t Qr = make_rsrc(Q + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Kr = make_rsrc(K + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Vr = make_rsrc(V + (size_t)bh * N * D, (uint32_t)N * D * 2);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int pr = w >> 1, wp = w & 1;
+  const int st = pr * S / NP, en = (pr + 1) * S / NP;  // this pair's run of the sequence
+  const float cs = fabsf(scale);
+  const float c = exp2_coef(scale);
+
+  bf16x8 qfA[DS], qfB[DS];
+  load_frags<D>(qfA, Qr, 64 * tA + 32 * wp + l32, g);
+  load_frags<D>(qfB, Qr, 64 * tB + 32 * wp + l32, g);
+  if (neg)
+#pragma unroll
+    for (int q = 0; q < DS; ++q) {
+      qfA[q] = negate(qfA[q]);
+      qfB[q] = negate(qfB[q]);
+    }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  float m = 0.f, l = 0.f;
+
+  // Park this wave's partial in a component-major record (consecutive lanes, consecutive
+  // words) and start a fresh one.
+  auto park = [&](float* rec) {
+    float* x = rec + wp * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[db][r];
+    x[16 * DB * 128] = m;
+    x[(16 * DB + 1) * 128] = l;
+  };
+  auto fetch = [&](int n, int b) {
+    const int k0 = (n < nA ? n : n - nA) * BK;
+    KTile::template load<2>(Kr, k0, kv[pr][b][0], wp, lane);
+    KTile::template load<2>(Vr, k0, kv[pr][b][1], wp, lane);
+  };
+
+  if (st < en) fetch(st, 0);
+  wait_vmem();
+  __syncthreads();
+  const int jmax = (S + NP - 1) / NP;
+  for (int j = 0; j < jmax; ++j) {
+    const int n = st + j;
+    const bool act = n < en;
+    const bf16* sK = kv[pr][j & 1][0];
+    const bf16* sV = kv[pr][j & 1][1];
+    // All of this step's LDS operands are requested before the next tile's direct loads
+    // (the compiler would otherwise wait for those loads ahead of the transposed reads).
+    bf16x8 vfr[4][DB], kfr[2][DS];
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(sV, 32 * db, 16 * u, lane);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(sK, 32 * kb + l32, 2 * q + g);
+    }
+    if (n + 1 < en) fetch(n + 1, (j & 1) ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (act) {
+      const bool isA = n < nA;
+      const int qt = isA ? tA : tB, kt = isA ? n : n - nA;
+      const bf16x8(&qf)[DS] = isA ? qfA : qfB;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = zero16();
+#pragma unroll
+        for (int q = 0; q < DS; ++q) sacc[kb] = mfma32(kfr[kb][q], qf[q], sacc[kb]);
+      }
+      if (kt == qt) mask_scores<2>(sacc, 0, 32 * wp + l32 - 4 * g);  // the diagonal tile
+      softmax_tile(sacc, m, l, o, c, n == st || n == nA);
+      bf16x8 pf[4];
+      p_operands(sacc, pf, l);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma32(vfr[u][db], pf[u], o[db]);
+      if (n + 1 == nA && n + 1 < en) {  // the run continues into B: park A's partial
+        park(park_cross);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = zero16();
+        m = 0.f;
+        l = 0.f;
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // Every pair parks its last partial (of A if its run ends within A, else of B) in slot pr.
+  float* slots = reinterpret_cast<float*>(&kv[0][0][0][0]);
+  if (st < en) park(slots + pr * XS * 128);
+  __syncthreads();
+  if (pr != 0 && pr != NP - 1) return;
+  const bool mergeA = pr == 0;
+  // Partials of the tile being merged: slot p holds tile A iff p's run ends within A; the
+  // crossing record holds A's part from the run that crosses into B, if one does.
+  auto included = [&](int p) {
+    const int sp = p * S / NP, ep = (p + 1) * S / NP;
+    return sp < ep && (ep <= nA) == mergeA;
+  };
+  bool cross = false;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int sp = p * S / NP, ep = (p + 1) * S / NP;
+    cross |= sp < nA && nA < ep;
+  }
+  cross = cross && mergeA;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if (included(p)) mm = fmaxf(mm, slots[p * XS * 128 + 16 * DB * 128 + wp * 64 + lane]);
+  if (cross) mm = fmaxf(mm, park_cross[16 * DB * 128 + wp * 64 + lane]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  auto add = [&](const float* rec) {
+    const float* x = rec + wp * 64 + lane;
+    const float f = fast_exp2((x[16 * DB * 128] - mm) * c);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] += f * x[(16 * db + r) * 128];
+    lsum += f * x[(16 * DB + 1) * 128];
+  };
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if (included(p)) add(slots + p * XS * 128);
+  if (cross) add(park_cross);
+  const float lt = halves_sum(lsum);
+  const int row = 64 * (mergeA ? tA : tB) + 32 * wp + l32;
+  store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
+  if (g == 0) Lout[(size_t)bh * N + row] = mm * cs + logf(lt);
 }
 
 // ----------------------------------------------------------------------------- backward
@@ -652,7 +827,7 @@ struct QRow {
     for (int s = 0; s < DS; ++s)
       dsum = dot_bf16x8(__builtin_bit_cast(u32x4, dof[s]), __builtin_bit_cast(u32x4, of[s]),
                         dsum);
-    dsum += swap_halves(dsum);
+    dsum = halves_sum(dsum);
     l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
     if (neg)
 #pragma unroll
@@ -989,9 +1164,14 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
   if constexpr (CAUSAL && D >= 32) {
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 128) * s.BH <= kNumCUs) {
       const long long grid = (long long)(s.Nq / 128) * s.BH;
-      hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+      if constexpr (D <= 64)
+        hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3((unsigned)grid), dim3(512), 0,
+                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
+                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+      else
+        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
+                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
       return hipGetLastError();
     }
   }

@@ -131,8 +131,35 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Value held by lane (lane ^ 32).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// v_permlane32_swap: {a, b} -> {a[0..31] ++ b[0..31], a[32..63] ++ b[32..63]} (lane ranges of
+// the two registers). Written as inline asm because hipcc 7.2 folds the second result of
+// __builtin_amdgcn_permlane32_swap into the first in reductions such as max(r0, r1), which
+// gives wrong results. The s_nop supplies the two wait states the instruction needs after a
+// VALU write of its operands (the compiler cannot see inside the asm to insert them).
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Value held by lane (lane ^ 32): a VALU op, no LDS round trip. With a = b = x, lane l < 32
+// finds x[l + 32] in b and lane l >= 32 finds x[l - 32] in a.
+__device__ __forceinline__ float swap_halves(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, (__lane_id() < 32) ? b : a);
+}
+// x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]) in every lane: after the swap a holds the lower
+// half's value and b the upper half's in every lane, so no lane select is needed and both
+// halves get the bitwise identical result.
+__device__ __forceinline__ float halves_sum(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
 
 // Workgroups are dispatched round-robin over the eight XCDs (workgroup b runs on XCD b % 8).
 // Give each XCD one contiguous range of logical tiles so that the tiles of a head, which
