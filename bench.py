@@ -98,7 +98,7 @@ def read_traffic(workload: str, kernel: str):
 def time_workload(w, steps, warmup):
     import torch
     from seeded_inputs import workload_inputs
-    from tiled_attention_causal_amd import fa_backward, fa_forward
+    from tiled_attention_causal_amd import backward_workspace_bytes, fa_backward, fa_forward
 
     dev = torch.device("cuda:0")
     inp = workload_inputs(w)
@@ -106,11 +106,12 @@ def time_workload(w, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, backward_workspace_bytes(q, k)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
         fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
-        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv)
+        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -130,7 +131,7 @@ def time_workload(w, steps, warmup):
         ev[i][0].record(stream)
         fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
         ev[i][1].record(stream)
-        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv)
+        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
         ev[i][2].record(stream)
     torch.cuda.synchronize(dev)
     fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)

@@ -98,8 +98,10 @@ FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, in
 
 /*
  * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs for these
- * sizes. The current kernels compute D = rowsum(dO o O) inside the backward kernel and
- * need none, so this returns 0; callers should still ask, and pass at least this much.
+ * sizes: for bf16, two floats per query row (B * H * Nq * 8 bytes), which hold the
+ * preprocessing step's per-row terms L log2(e) and -D; for fp32, 0. Returns 0 for sizes
+ * fa_backward would reject. The caller owns the workspace; its contents need no
+ * initialisation and are meaningless after the call.
  */
 FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
                                    int64_t Nk, int64_t d);
@@ -107,11 +109,12 @@ FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, 
 /*
  * fa_backward -- dQ, dK, dV of O = softmax(Q K^T * scale [+ causal mask]) V.
  *
- * Follows problem flash_backward and the two-pass split of section 1.3.3: P is rebuilt as
- * exp(S - L) from Q, K and the forward's L; D_i = sum_k dO_ik O_ik; one set of workgroups
- * walks query tiles for each key tile and accumulates dK and dV, another walks key tiles
- * for each query tile and accumulates dQ, so no output is ever updated atomically and the
- * result is bitwise deterministic. The scale appears once in dQ and once in dK.
+ * Follows problem flash_backward and the two-pass split of section 1.3.3: a preprocessing
+ * kernel forms D_i = sum_k dO_ik O_ik (and L_i log2(e)) per query row in the workspace; the
+ * main kernel rebuilds P as exp(S - L) from Q, K and the forward's L; one set of its
+ * workgroups walks query tiles for each key tile and accumulates dK and dV, another walks
+ * key tiles for each query tile and accumulates dQ, so no output is ever updated atomically
+ * and the result is bitwise deterministic. The scale appears once in dQ and once in dK.
  *
  *   Q, K, V, is_causal, scale   exactly as given to fa_forward
  *   O, L                        fa_forward's outputs for those inputs
@@ -119,7 +122,9 @@ FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, 
  *   dQ                          [B,H,Nq,d] dtype, written
  *   dK, dV                      [B,H,Nk,d] dtype, written
  *   workspace, workspace_bytes  device scratch of at least fa_backward_workspace_bytes()
- *                               bytes (may be NULL when that is 0)
+ *                               bytes, 4-byte aligned (may be NULL when that is 0); it must
+ *                               not overlap any other argument, and calls that share one
+ *                               workspace must not run concurrently
  *   stream                      hipStream_t or NULL
  */
 FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,

@@ -56,9 +56,14 @@ def test_status_strings(lib):
     assert lib.fa_status_string(77).decode() == "FA_UNKNOWN_STATUS"
 
 
-def test_workspace_is_zero(lib):
-    for dt in (0, 1):
-        assert lib.fa_backward_workspace_bytes(dt, 8, 1, 4096, 4096, 64) == 0
+def test_workspace_sizes(lib):
+    # bf16: L log2(e) and -D per query row; fp32: none; rejected sizes report 0.
+    assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 64) == 8 * 4096 * 8
+    assert lib.fa_backward_workspace_bytes(1, 4, 25, 2048, 1024, 128) == 100 * 2048 * 8
+    assert lib.fa_backward_workspace_bytes(1, 2, 3, 0, 64, 64) == 0
+    assert lib.fa_backward_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 0
+    assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 48) == 0
+    assert lib.fa_backward_workspace_bytes(1, -1, 1, 4096, 4096, 64) == 0
 
 
 # A fake, 16-byte aligned address. Only passed where validation must fail first (or where
@@ -73,7 +78,7 @@ def fwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, causal=1, s
 
 
 def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
-        causal=1, scale=0.125, dq=P, dk=P, dv=P, ws=None, ws_bytes=0):
+        causal=1, scale=0.125, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 30):
     return lib.fa_backward(dtype, B, H, Nq, Nk, d, q, k, v, o, lse, do, causal, scale, dq, dk,
                            dv, ws, ws_bytes, None)
 
@@ -106,6 +111,7 @@ def test_forward_empty_is_a_noop(lib, kw):
     (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
     (dict(dv=None), 1), (dict(dk=BAD), 1),
     (dict(Nq=0, dk=None), 1),  # Nq == 0 still writes dK and dV
+    (dict(ws_bytes=128 * 8 - 1), 1), (dict(ws=None), 1), (dict(ws=P + 2), 1),
 ])
 def test_backward_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
@@ -113,6 +119,7 @@ def test_backward_rejects(lib, kw, code):
 
 def test_backward_empty_is_a_noop(lib):
     assert bwd(lib, B=0) == 0
+    assert bwd(lib, B=0, ws=None, ws_bytes=0) == 0
     assert bwd(lib, Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None,
                dk=None, dv=None) == 0
 

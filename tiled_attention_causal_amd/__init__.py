@@ -3,7 +3,8 @@
     from tiled_attention_causal_amd import fa_forward, fa_backward, FlashAttention
 """
 from ._lib import FAError, LIB_PATH, load  # noqa: F401
-from .ops import FlashAttention, default_scale, fa_backward, fa_forward  # noqa: F401
+from .ops import (FlashAttention, backward_workspace_bytes, default_scale,  # noqa: F401
+                  fa_backward, fa_forward)
 
-__all__ = ["fa_forward", "fa_backward", "FlashAttention", "default_scale", "FAError", "load",
-           "LIB_PATH"]
+__all__ = ["fa_forward", "fa_backward", "backward_workspace_bytes", "FlashAttention",
+           "default_scale", "FAError", "load", "LIB_PATH"]

@@ -61,8 +61,12 @@ const char* fa_status_string(fa_status status) {
   return "FA_UNKNOWN_STATUS";
 }
 
-size_t fa_backward_workspace_bytes(fa_dtype, int64_t, int64_t, int64_t, int64_t, int64_t) {
-  return 0;
+size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                   int64_t d) {
+  fa::Shape s;
+  if (check_common(dtype, B, H, Nq, Nk, d, 1.f, 0, &s) != FA_SUCCESS) return 0;
+  // bf16: L log2(e) and -D per query row (two floats); the fp32 path needs nothing.
+  return dtype == FA_DTYPE_BF16 ? (size_t)s.BH * (size_t)s.Nq * 2 * sizeof(float) : 0;
 }
 
 fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
@@ -94,9 +98,10 @@ fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t 
   fa::Shape s;
   const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
   if (st != FA_SUCCESS) return st;
-  if (workspace_bytes < fa_backward_workspace_bytes(dtype, B, H, Nq, Nk, d))
+  const size_t ws_need = fa_backward_workspace_bytes(dtype, B, H, Nq, Nk, d);
+  if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
+  if (ws_need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
     return FA_ERROR_INVALID_VALUE;
-  (void)workspace;
   const bool has_q = (int64_t)s.BH * Nq > 0, has_k = (int64_t)s.BH * Nk > 0;
   if (!has_q && !has_k) return FA_SUCCESS;
   if (has_q && Nk == 0) return FA_ERROR_INVALID_VALUE;  // softmax over no keys
@@ -108,7 +113,8 @@ fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t 
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
-    e = fa::launch_bwd_bf16(s, Q, K, V, O, L, dO, dQ, dK, dV, hs);
+    e = fa::launch_bwd_bf16(s, Q, K, V, O, L, dO, dQ, dK, dV, static_cast<float*>(workspace),
+                            hs);
   else
     e = fa::launch_bwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
                            static_cast<const float*>(V), static_cast<const float*>(O), L,

@@ -21,6 +21,8 @@
 // are then per lane, plus one exchange with lane ^ 32. The second product of each pass
 // (P V, P^T dO, dS^T Q, dS K) takes the score registers directly as its B operand and reads
 // its LDS operand transposed (Tile::tfrag).
+#include <algorithm>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -648,64 +650,65 @@ struct Bwd {
   static constexpr int DS = D / 16, DB = (D + 31) / 32;
   using MTile = Tile<32, D>;
   static constexpr int T = MTile::ELEMS;
-  // dK/dV stream buffer: Q, dO, O tiles, then 32 floats L (turned into L log2e in place) and
-  // 32 floats D.
-  static constexpr int KV_BUF = 3 * T + 2 * 32 * 2;
+  // dK/dV stream buffer: Q and dO tiles, then 32 floats L log2e and 32 floats -D (written by
+  // bwd_prep_kernel).
+  static constexpr int KV_BUF = 2 * T + 2 * 32 * 2;
   // dQ stream buffer: K, V tiles.
   static constexpr int Q_BUF = 2 * T;
   static constexpr int NCH = D / 8;
 };
 
-__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float acc) {
+// Per-row terms of the backward, one launch ahead of bwd_kernel: L2 = L log2(e) (the
+// exponent offset of P = exp2(S scale log2(e) - L2)) and ND = -D with D = rowsum(dO o O)
+// (problem flash_backward's preprocessing). ND starts the dP accumulators, so dS = P (dP - D)
+// is one multiply. D_CH = d/8 lanes share a row, one 16-byte chunk of dO and of O each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ O,
+                                                       const bf16* __restrict__ dO,
+                                                       const float* __restrict__ L,
+                                                       float* __restrict__ L2,
+                                                       float* __restrict__ ND, long long rows) {
+  constexpr int CH = D / 8;
+  const long long total = rows * CH;
+  // Block-uniform stride loop: the grid is capped so its work-item count fits 32 bits, and
+  // lane groups of one row stay together (CH divides 256).
+  for (long long base = (long long)blockIdx.x * 256; base < total;
+       base += (long long)gridDim.x * 256) {
+    const long long t = base + threadIdx.x;
+    const long long row = t / CH;
+    const int ch = (int)(t % CH);
+    // Lanes past the last row re-read it instead of branching around the loads: the lane
+    // reduction below then follows straight-line code with the full wave active.
+    const long long r = row < rows ? row : rows - 1;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(dO + r * D + ch * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(O + r * D + ch * 8);
+    float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc = dot2_bf16(a[i], b[i], acc);
-  return acc;
-}
-
-// D = rowsum(dO o O) and L log2e for the 32 staged rows m0.. of a dK/dV stream buffer, by the
-// NTHR threads t = 0 .. NTHR-1 that share the buffer (rows >= Nq get L log2e = +inf, so their
-// P is 0). The caller synchronises before the values are read.
-template <int D, int NTHR>
-__device__ __forceinline__ void kv_stage_rows(bf16* buf, int m0, int Nq, int t) {
-  using B = Bwd<D>;
-  constexpr int CPT = (32 * B::NCH + NTHR - 1) / NTHR;  // chunks per thread
-  constexpr int TPR = B::NCH / CPT;                     // threads per row
-  const bf16* sdO = buf + B::T;
-  const bf16* sO = buf + 2 * B::T;
-  float* sL2 = reinterpret_cast<float*>(buf + 3 * B::T);
-  float* sD = sL2 + 32;
-  const int row = t / TPR, part = t % TPR;
-  float dsum = 0.f;
-  if (row < 32) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = part * CPT + i;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sdO + swz<B::NCH>(row, ch));
-      const u32x4 b = *reinterpret_cast<const u32x4*>(sO + swz<B::NCH>(row, ch));
-      dsum = dot_bf16x8(a, b, dsum);
+    for (int i = 0; i < 4; ++i) acc = dot2_bf16(a[i], b[i], acc);
+    acc = group_sum<CH>(acc);
+    if (row < rows && ch == 0) {
+      L2[row] = L[row] * kLog2e;
+      ND[row] = -acc;
     }
   }
-  dsum = group_sum<TPR>(dsum);
-  if (row < 32 && part == 0) {
-    sD[row] = dsum;
-    sL2[row] = m0 + row < Nq ? sL2[row] * kLog2e : INFINITY;
-  }
 }
 
-// Direct loads of the dK/dV stream for moving tile m0.. (Q, dO, O rows and L) into `buf`,
-// by NW waves (index w).
+// Direct loads of the dK/dV stream for moving tile m0.. (Q and dO rows, L2 and ND) into
+// `buf`, by NW >= 2 waves (index w). Rows past Nq read as zeros: their Q, dO and ND are 0, so
+// their P = exp2(0) = 1 meets dO = 0 and dP - D = 0 and adds nothing to dV or dK.
 template <int D, int NW>
-__device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t Or, rsrc_t Lr, int m0,
+__device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr, int m0,
                                          bf16* buf, int w, int lane) {
+  static_assert(NW >= 2, "L2 and ND are fetched by waves 0 and 1");
   using B = Bwd<D>;
   B::MTile::template load<NW>(Qr, m0, buf, w, lane);
   B::MTile::template load<NW>(dOr, m0, buf + B::T, w, lane);
-  B::MTile::template load<NW>(Or, m0, buf + 2 * B::T, w, lane);
-  if (w == 0 && lane < 32) dma4(Lr, (uint32_t)(m0 + lane) * 4, buf + 3 * B::T);
+  if (w < 2 && lane < 32)
+    dma4(w == 0 ? L2r : NDr, (uint32_t)(m0 + lane) * 4, buf + 2 * B::T + 64 * w);
 }
 
-// dK/dV step, first half: S = Q K^T and dP = dO V^T for the 32 staged queries against this
-// wave's 32 keys (kf, vf). Layout: lane = key, register r = query 8(r/4) + 4g + r%4.
+// dK/dV step, first half: S = Q K^T and dP - D = dO V^T - D for the 32 staged queries against
+// this wave's 32 keys (kf, vf). Layout: lane = key, register r = query 8(r/4) + 4g + r%4.
 template <int D>
 __device__ __forceinline__ void kv_scores_mfma(const bf16* buf, const bf16x8 (&kf)[D / 16],
                                                const bf16x8 (&vf)[D / 16], f32x16& sp,
@@ -717,8 +720,16 @@ __device__ __forceinline__ void kv_scores_mfma(const bf16* buf, const bf16x8 (&k
     qa[s] = B::MTile::frag(buf, l32, 2 * s + g);
     da[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
+  // dP starts at -D of its query row (register r: query 8(r/4) + 4g + r%4), so the MFMAs
+  // leave dP - D.
+  const float* sND = reinterpret_cast<const float*>(buf + 2 * B::T) + 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 n4 = *reinterpret_cast<const f32x4*>(sND + 8 * j + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dp[4 * j + i] = n4[i];
+  }
   sp = zero16();
-  dp = zero16();
 #pragma unroll
   for (int s = 0; s < B::DS; ++s) {
     sp = mfma32(qa[s], kf[s], sp);
@@ -726,7 +737,7 @@ __device__ __forceinline__ void kv_scores_mfma(const bf16* buf, const bf16x8 (&k
   }
 }
 
-// dK/dV step, second half: P = exp2(S c - L log2e), dS = P (dP - D), then dV^T += dO^T P and
+// dK/dV step, second half: P = exp2(S c - L2), dS = P (dP - D), then dV^T += dO^T P and
 // dK^T += Q^T dS (lane = key, register = column of d). When `masked`, queries with offset
 // 8(r/4) + r%4 below `lim` (earlier than this lane's key) get P = dS = 0. The next tile's
 // direct loads were issued before this step's LDS reads, so the compiler waits for them
@@ -743,17 +754,16 @@ __device__ __forceinline__ void kv_update(const bf16* buf, f32x16& sp, f32x16& d
     mask_scores<1>(t, lim, 1 << 30);
     sp = t[0];
   }
-  const float* sL2 = reinterpret_cast<const float*>(buf + 3 * B::T);
+  const float* sL2 = reinterpret_cast<const float*>(buf + 2 * B::T);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 8 * j + 4 * g);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sL2 + 32 + 8 * j + 4 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * j + i;
       const float p = fast_exp2(fmaf(sp[r], c, -l4[i]));
       sp[r] = p;
-      dp[r] = p * (dp[r] - d4[i]);
+      dp[r] = p * dp[r];
     }
   }
 #pragma unroll
@@ -770,14 +780,14 @@ __device__ __forceinline__ void kv_update(const bf16* buf, f32x16& sp, f32x16& d
   }
 }
 
-// dQ step: S^T = K Q^T, dP^T = V dO^T (lane = query, register r = key 8(r/4) + 4g + r%4),
-// P = exp2(S c - L log2e), dS = P (dP - D), dQ^T += K^T dS^T. When `masked`, keys with
-// offset above hi get P = dS = 0.
+// dQ step: S^T = K Q^T, dP^T - D = V dO^T - D (lane = query, register r = key
+// 8(r/4) + 4g + r%4), P = exp2(S c - L2), dS = P (dP - D), dQ^T += K^T dS^T. When `masked`,
+// keys with offset above hi get P = dS = 0.
 template <int D>
 __device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D / 16],
                                          const bf16x8 (&dof)[D / 16],
                                          f32x16 (&dqt)[(D + 31) / 32], float c, float l2,
-                                         float dsum, bool masked, int hi, int lane, int l32,
+                                         float nd, bool masked, int hi, int lane, int l32,
                                          int g) {
   using B = Bwd<D>;
   constexpr int DS = B::DS, DB = B::DB;
@@ -787,7 +797,9 @@ __device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D /
     k[s] = B::MTile::frag(buf, l32, 2 * s + g);
     v[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
-  f32x16 st[1] = {zero16()}, dpt = zero16();
+  f32x16 st[1] = {zero16()}, dpt;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dpt[r] = nd;  // dP starts at -D of this lane's query
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     st[0] = mfma32(k[s], qf[s], st[0]);
@@ -797,7 +809,7 @@ __device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D /
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float p = fast_exp2(fmaf(st[0][r], c, -l2));
-    dpt[r] = p * (dpt[r] - dsum);
+    dpt[r] = p * dpt[r];
   }
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
@@ -808,27 +820,20 @@ __device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D /
   }
 }
 
-// Stationary state of a dQ wave: Q and dO fragments of query row `qrow`, its L log2e and D.
+// Stationary state of a dQ wave: Q and dO fragments of query row `qrow`, its L2 and ND
+// (rows past Nq read zeros and are never stored).
 template <int D>
 struct QRow {
   bf16x8 qf[D / 16], dof[D / 16];
-  float l2, dsum;
-  __device__ __forceinline__ void load(rsrc_t Qr, rsrc_t dOr, rsrc_t Or, rsrc_t Lr, int qrow,
-                                       int Nq, int g, int neg) {
+  float l2, nd;
+  __device__ __forceinline__ void load(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr, int qrow,
+                                       int g, int neg) {
     constexpr int DS = D / 16;
-    bf16x8 of[DS];
     load_frags<D>(qf, Qr, qrow, g);
     load_frags<D>(dof, dOr, qrow, g);
-    load_frags<D>(of, Or, qrow, g);
-    const float lrow = buf_load_f32(Lr, qrow * 4);
+    l2 = buf_load_f32(L2r, qrow * 4);
+    nd = buf_load_f32(NDr, qrow * 4);
     wait_vmem();
-    dsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < DS; ++s)
-      dsum = dot_bf16x8(__builtin_bit_cast(u32x4, dof[s]), __builtin_bit_cast(u32x4, of[s]),
-                        dsum);
-    dsum = halves_sum(dsum);
-    l2 = qrow < Nq ? lrow * kLog2e : INFINITY;
     if (neg)
 #pragma unroll
       for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
@@ -848,8 +853,9 @@ __device__ __forceinline__ void load_kv_rows(bf16x8 (&kf)[D / 16], bf16x8 (&vf)[
 
 // dK, dV for the 128 keys starting at k0 of one head (4 waves share one query stream).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
-                                          rsrc_t Lr, rsrc_t dOr, bf16* dKh, bf16* dVh, int k0,
+__device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr,
+                                          rsrc_t L2r, rsrc_t NDr, rsrc_t dOr, bf16* dKh,
+                                          bf16* dVh, int k0,
                                           int Nq, int Nk, float scale, int neg) {
   using B = Bwd<D>;
   constexpr int DS = B::DS, DB = B::DB;
@@ -869,7 +875,7 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
 
   const int nmt = (Nq + 31) / 32;
   const int mt0 = CAUSAL ? k0 / 32 : 0;
-  if (mt0 < nmt) kv_fetch<D, 4>(Qr, dOr, Or, Lr, mt0 * 32, smem, w, lane);
+  if (mt0 < nmt) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, mt0 * 32, smem, w, lane);
   wait_vmem();
   __syncthreads();
   for (int mt = mt0; mt < nmt; ++mt) {
@@ -877,13 +883,12 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
     bf16* nbuf = smem + (((mt - mt0) & 1) ^ 1) * B::KV_BUF;
     const int m0 = mt * 32;
     const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
-    if (mt + 1 < nmt) kv_fetch<D, 4>(Qr, dOr, Or, Lr, m0 + 32, nbuf, w, lane);
-    f32x16 sp, dp;
-    if (active) kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
-    kv_stage_rows<D, 256>(buf, m0, Nq, tid);
-    __syncthreads();
-    if (active)
+    if (mt + 1 < nmt) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, m0 + 32, nbuf, w, lane);
+    if (active) {
+      f32x16 sp, dp;
+      kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
       kv_update<D>(buf, sp, dp, dvt, dkt, c, CAUSAL && m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
+    }
     wait_vmem();
     __syncthreads();
   }
@@ -896,8 +901,9 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
 
 // dQ for the 128 queries starting at q0 of one head (4 waves share one key stream).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
-                                        rsrc_t Lr, rsrc_t dOr, bf16* dQh, int q0, int Nq, int Nk,
+__device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr,
+                                        rsrc_t L2r, rsrc_t NDr, rsrc_t dOr, bf16* dQh, int q0,
+                                        int Nq, int Nk,
                                         float scale, int neg) {
   using B = Bwd<D>;
   constexpr int DB = B::DB;
@@ -907,7 +913,7 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
   const float c = exp2_coef(scale);
 
   QRow<D> row;
-  row.load(Qr, dOr, Or, Lr, qrow, Nq, g, neg);
+  row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
   f32x16 dqt[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqt[db] = zero16();
@@ -930,7 +936,7 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
       B::MTile::template load<4>(Vr, n0 + 32, nbuf + B::T, w, lane);
     }
     if (active)
-      q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.dsum,
+      q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.nd,
                   (CAUSAL && n0 + 31 > qw0) || n0 + 32 > Nk,
                   min(CAUSAL ? qrow - n0 - 4 * g : 1 << 30, Nk - 1 - n0 - 4 * g), lane, l32, g);
     wait_vmem();
@@ -947,8 +953,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
                                                   const bf16* __restrict__ V,
-                                                  const bf16* __restrict__ O,
-                                                  const float* __restrict__ L,
+                                                  const float* __restrict__ L2,
+                                                  const float* __restrict__ ND,
                                                   const bf16* __restrict__ dO,
                                                   bf16* __restrict__ dQ, bf16* __restrict__ dK,
                                                   bf16* __restrict__ dV, int Nq, int Nk,
@@ -961,16 +967,16 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
   const int bh = lid / per_head, idx = lid % per_head;
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
   const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
-  const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq);
-  const rsrc_t dOr = make_rsrc(dO + oq, bq);
+  const rsrc_t Qr = make_rsrc(Q + oq, bq), dOr = make_rsrc(dO + oq, bq);
   const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
-  const rsrc_t Lr = make_rsrc(L + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const rsrc_t L2r = make_rsrc(L2 + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const rsrc_t NDr = make_rsrc(ND + (size_t)bh * Nq, (uint32_t)Nq * 4);
   if (idx < nkv) {
-    dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, idx * 128, Nq, Nk,
+    dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dK + ok, dV + ok, idx * 128, Nq, Nk,
                          scale, neg);
   } else {
     const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
-    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
+    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
   }
 }
 
@@ -988,7 +994,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
 template <int D>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ O, const float* __restrict__ L, const bf16* __restrict__ dO,
+    const float* __restrict__ L2, const float* __restrict__ ND, const bf16* __restrict__ dO,
     bf16* __restrict__ dQ, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale,
     int neg) {
   using B = Bwd<D>;
@@ -1001,12 +1007,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
   const int bh = lid / T, idx = lid % T;
   const size_t o = (size_t)bh * N * D;
   const uint32_t nb = (uint32_t)N * D * 2;
-  const rsrc_t Qr = make_rsrc(Q + o, nb), Or = make_rsrc(O + o, nb), dOr = make_rsrc(dO + o, nb);
+  const rsrc_t Qr = make_rsrc(Q + o, nb), dOr = make_rsrc(dO + o, nb);
   const rsrc_t Kr = make_rsrc(K + o, nb), Vr = make_rsrc(V + o, nb);
-  const rsrc_t Lr = make_rsrc(L + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t L2r = make_rsrc(L2 + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t NDr = make_rsrc(ND + (size_t)bh * N, (uint32_t)N * 4);
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
-  const int pr = w >> 1, wp = w & 1, pt = tid & 127;  // pair, wave in pair, thread in pair
+  const int pr = w >> 1, wp = w & 1;  // pair, wave in pair
   const float c = exp2_coef(scale);
   const int nsteps = T + 1;
   constexpr int XS = 2 * 16 * DB;  // merge record per lane: up to two accumulator sets
@@ -1030,7 +1037,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
       dvt[db] = zero16();
       dkt[db] = zero16();
     }
-    kv_fetch<D, 2>(Qr, dOr, Or, Lr, 32 * mt_of(0), smem[pr][0], wp, lane);
+    kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(0), smem[pr][0], wp, lane);
     wait_vmem();
     __syncthreads();
     for (int n = 0; n < nsteps; ++n) {
@@ -1039,13 +1046,12 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
       const int m0 = 32 * mt_of(n);
       const int kw0 = 64 * kt + 32 * wp;
       const bool active = m0 + 31 >= kw0;
-      if (n + 1 < nsteps) kv_fetch<D, 2>(Qr, dOr, Or, Lr, 32 * mt_of(n + 1), nbuf, wp, lane);
-      f32x16 sp, dp;
-      if (active) kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
-      kv_stage_rows<D, 128>(buf, m0, N, pt);
-      __syncthreads();
-      if (active)
+      if (n + 1 < nsteps) kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n + 1), nbuf, wp, lane);
+      if (active) {
+        f32x16 sp, dp;
+        kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
         kv_update<D>(buf, sp, dp, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
+      }
       if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
         store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
         store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
@@ -1100,7 +1106,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     int qt = qt_of(0);
     int qrow = 64 * qt + 32 * wp + l32;
     QRow<D> row;
-    row.load(Qr, dOr, Or, Lr, qrow, N, g, neg);
+    row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
     f32x16 dqt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = zero16();
@@ -1119,7 +1125,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
         B::MTile::template load<2>(Vr, 32 * kt_of(n + 1), nbuf + B::T, wp, lane);
       }
       if (active)
-        q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.dsum, n0 + 31 > qw0,
+        q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
                     qrow - n0 - 4 * g, lane, l32, g);
       if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
         store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
@@ -1127,7 +1133,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
         for (int db = 0; db < DB; ++db) dqt[db] = zero16();
         qt = tA;
         qrow = 64 * qt + 32 * wp + l32;
-        row.load(Qr, dOr, Or, Lr, qrow, N, g, neg);
+        row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
       }
       wait_vmem();
       __syncthreads();
@@ -1185,8 +1191,19 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
 
 template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* O,
-                 const float* L, const void* dO, void* dQ, void* dK, void* dV,
+                 const float* L, const void* dO, void* dQ, void* dK, void* dV, float* ws,
                  hipStream_t stream) {
+  // Workspace: L2 for the B*H*Nq rows, then ND for the same rows.
+  const long long rows = (long long)s.BH * s.Nq;
+  float* L2 = ws;
+  float* ND = ws + rows;
+  if (rows > 0) {
+    const long long prep_grid = std::min((rows * (D / 8) + 255) / 256, 1LL << 16);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_grid), dim3(256), 0, stream,
+                       (const bf16*)O, (const bf16*)dO, L, L2, ND, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
   // the longest tile on the critical path of a small grid; see bwd_causal_paired_kernel.
   // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
@@ -1195,17 +1212,16 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 2 * kNumCUs) {
       const long long grid = (long long)(s.Nq / 64) * s.BH;
       hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)O,
-                         L, (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
+                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
+                         (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
                          s.scale < 0.f ? 1 : 0);
       return hipGetLastError();
     }
   }
   const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH;
   hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)O, L,
-                     (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.Nk, s.scale,
-                     s.scale < 0.f ? 1 : 0);
+                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND, (const bf16*)dO,
+                     (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.Nk, s.scale, s.scale < 0.f ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1230,11 +1246,11 @@ hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const v
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* O, const float* L, const void* dO, void* dQ, void* dK,
-                           void* dV, hipStream_t stream) {
-#define FA_BWD(DD)                                                                   \
-  case DD:                                                                           \
-    return s.causal ? bwd_t<DD, true>(s, Q, K, V, O, L, dO, dQ, dK, dV, stream)      \
-                    : bwd_t<DD, false>(s, Q, K, V, O, L, dO, dQ, dK, dV, stream);
+                           void* dV, float* workspace, hipStream_t stream) {
+#define FA_BWD(DD)                                                                            \
+  case DD:                                                                                    \
+    return s.causal ? bwd_t<DD, true>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace, stream)    \
+                    : bwd_t<DD, false>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace, stream);
   switch (s.d) {
     FA_BWD(16)
     FA_BWD(32)

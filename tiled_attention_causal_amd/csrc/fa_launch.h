@@ -17,9 +17,11 @@ struct Shape {
 
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V, void* O,
                            float* L, hipStream_t stream);
+// `workspace` holds 2 * BH * Nq floats: per-row terms written by the first of the two kernels
+// this launches and read by the second.
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* O, const float* L, const void* dO, void* dQ, void* dK,
-                           void* dV, hipStream_t stream);
+                           void* dV, float* workspace, hipStream_t stream);
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           float* O, float* L, hipStream_t stream);
 hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const float* V,

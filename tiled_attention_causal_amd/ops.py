@@ -74,8 +74,12 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: boo
 def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                 lse: torch.Tensor, do: torch.Tensor, is_causal: bool = False,
                 scale: float | None = None, dq: torch.Tensor | None = None,
-                dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
-    """dQ, dK, dV of the attention forward, from Q, K, V, O, L and dO."""
+                dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """dQ, dK, dV of the attention forward, from Q, K, V, O, L and dO.
+
+    `workspace`, if given, is a device tensor of at least backward_workspace_bytes() bytes
+    that the call may overwrite; otherwise one is allocated."""
     lib = _lib.load()
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -91,7 +95,12 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     for name, t, n in (("dq", dq, Nq), ("dk", dk, Nk), ("dv", dv, Nk)):
         _check(name, t, (B, H, n, d), dt, q.device)
     ws_bytes = lib.fa_backward_workspace_bytes(_DTYPES[dt], B, H, Nq, Nk, d)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if workspace is not None:
+        if workspace.device != q.device or workspace.nbytes < ws_bytes:
+            raise ValueError(f"workspace must be a {ws_bytes}-byte tensor on {q.device}")
+        ws, ws_bytes = workspace, workspace.nbytes
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     sc = default_scale(d) if scale is None else float(scale)
     st = lib.fa_backward(_DTYPES[dt], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                          o.data_ptr(), lse.data_ptr(), do.data_ptr(), int(bool(is_causal)), sc,
@@ -99,6 +108,12 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q))
     _raise(st, "fa_backward")
     return dq, dk, dv
+
+
+def backward_workspace_bytes(q: torch.Tensor, k: torch.Tensor) -> int:
+    """Bytes of workspace fa_backward needs for these query and key tensors."""
+    B, H, Nq, d = q.shape
+    return _lib.load().fa_backward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, k.shape[2], d)
 
 
 class FlashAttention(torch.autograd.Function):
