@@ -707,54 +707,67 @@ __device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc
     dma4(w == 0 ? L2r : NDr, (uint32_t)(m0 + lane) * 4, buf + 2 * B::T + 64 * w);
 }
 
-// dK/dV step, first half: S = Q K^T and dP - D = dO V^T - D for the 32 staged queries against
-// this wave's 32 keys (kf, vf). Layout: lane = key, register r = query 8(r/4) + 4g + r%4.
+// Transposed LDS operands of one dK/dV step (dO^T and Q^T, the A operands of dV^T and dK^T).
+// The paired kernel requests them at the start of the step, before the next tile's direct
+// loads are issued: the compiler cannot tell that those loads do not alias a transposed read,
+// and would otherwise wait for them to land first. That costs 8 * DB registers for the whole
+// step, which bwd_kernel cannot afford without dropping from three waves per SIMD to two, so
+// there kv_step reads them where they are used (EARLY = false) and takes the wait, which the
+// first half of the step overlaps. Plain LDS reads do not have this problem.
 template <int D>
-__device__ __forceinline__ void kv_scores_mfma(const bf16* buf, const bf16x8 (&kf)[D / 16],
-                                               const bf16x8 (&vf)[D / 16], f32x16& sp,
-                                               f32x16& dp, int l32, int g) {
-  using B = Bwd<D>;
-  bf16x8 qa[B::DS], da[B::DS];
+struct KvOps {
+  static constexpr int DB = (D + 31) / 32;
+  bf16x8 dot[2][DB], qt[2][DB];
+  __device__ __forceinline__ void read(const bf16* buf, int lane) {
+    using B = Bwd<D>;
 #pragma unroll
-  for (int s = 0; s < B::DS; ++s) {
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dot[st][db] = B::MTile::tfrag(buf + B::T, 32 * db, 16 * st, lane);
+        qt[st][db] = B::MTile::tfrag(buf, 32 * db, 16 * st, lane);
+      }
+  }
+};
+
+// One dK/dV step for the 32 staged queries against this wave's 32 keys (kf, vf):
+// S = Q K^T and dP - D = dO V^T - D (the dP accumulator starts at -D), with lane = key and
+// register r = query 8(r/4) + 4g + r%4; P = exp2(S c - L2), dS = P (dP - D); then
+// dV^T += dO^T P and dK^T += Q^T dS (lane = key, register = column of d). When `masked`,
+// queries with offset 8(r/4) + r%4 below `lim` (earlier than this lane's key) get P = dS = 0.
+template <int D, bool EARLY>
+__device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
+                                        const bf16x8 (&kf)[D / 16],
+                                        const bf16x8 (&vf)[D / 16],
+                                        f32x16 (&dvt)[(D + 31) / 32],
+                                        f32x16 (&dkt)[(D + 31) / 32], float c, bool masked,
+                                        int lim, int lane, int l32, int g) {
+  using B = Bwd<D>;
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
+  bf16x8 qa[DS], da[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
     qa[s] = B::MTile::frag(buf, l32, 2 * s + g);
     da[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
-  // dP starts at -D of its query row (register r: query 8(r/4) + 4g + r%4), so the MFMAs
-  // leave dP - D.
-  const float* sND = reinterpret_cast<const float*>(buf + 2 * B::T) + 32;
+  const float* sL2 = reinterpret_cast<const float*>(buf + 2 * B::T);
+  f32x16 sp = zero16(), dp;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const f32x4 n4 = *reinterpret_cast<const f32x4*>(sND + 8 * j + 4 * g);
+    const f32x4 n4 = *reinterpret_cast<const f32x4*>(sL2 + 32 + 8 * j + 4 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dp[4 * j + i] = n4[i];
   }
-  sp = zero16();
 #pragma unroll
-  for (int s = 0; s < B::DS; ++s) {
+  for (int s = 0; s < DS; ++s) {
     sp = mfma32(qa[s], kf[s], sp);
     dp = mfma32(da[s], vf[s], dp);
   }
-}
-
-// dK/dV step, second half: P = exp2(S c - L2), dS = P (dP - D), then dV^T += dO^T P and
-// dK^T += Q^T dS (lane = key, register = column of d). When `masked`, queries with offset
-// 8(r/4) + r%4 below `lim` (earlier than this lane's key) get P = dS = 0. The next tile's
-// direct loads were issued before this step's LDS reads, so the compiler waits for them
-// ahead of the transposed reads below; that latency overlaps the first half of the step.
-template <int D>
-__device__ __forceinline__ void kv_update(const bf16* buf, f32x16& sp, f32x16& dp,
-                                          f32x16 (&dvt)[(D + 31) / 32],
-                                          f32x16 (&dkt)[(D + 31) / 32], float c, bool masked,
-                                          int lim, int lane, int g) {
-  using B = Bwd<D>;
-  constexpr int DB = B::DB;
   if (masked) {  // queries with offset below lim are earlier than this lane's key
     f32x16 t[1] = {sp};
     mask_scores<1>(t, lim, 1 << 30);
     sp = t[0];
   }
-  const float* sL2 = reinterpret_cast<const float*>(buf + 2 * B::T);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL2 + 8 * j + 4 * g);
@@ -772,25 +785,43 @@ __device__ __forceinline__ void kv_update(const bf16* buf, f32x16& sp, f32x16& d
     const bf16x8 sf = to_bf16x8(dp, 8 * st);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const bf16x8 dot = B::MTile::tfrag(buf + B::T, 32 * db, 16 * st, lane);
-      const bf16x8 qt = B::MTile::tfrag(buf, 32 * db, 16 * st, lane);
-      dvt[db] = mfma32(dot, pf, dvt[db]);
-      dkt[db] = mfma32(qt, sf, dkt[db]);
+      if constexpr (EARLY) {
+        dvt[db] = mfma32(op.dot[st][db], pf, dvt[db]);
+        dkt[db] = mfma32(op.qt[st][db], sf, dkt[db]);
+      } else {
+        dvt[db] = mfma32(B::MTile::tfrag(buf + B::T, 32 * db, 16 * st, lane), pf, dvt[db]);
+        dkt[db] = mfma32(B::MTile::tfrag(buf, 32 * db, 16 * st, lane), sf, dkt[db]);
+      }
     }
   }
 }
 
+// Transposed LDS operands of one dQ step (K^T), requested early or late as in KvOps.
+template <int D>
+struct QOps {
+  static constexpr int DB = (D + 31) / 32;
+  bf16x8 kt[2][DB];
+  __device__ __forceinline__ void read(const bf16* buf, int lane) {
+    using B = Bwd<D>;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) kt[s2][db] = B::MTile::tfrag(buf, 32 * db, 16 * s2, lane);
+  }
+};
+
 // dQ step: S^T = K Q^T, dP^T - D = V dO^T - D (lane = query, register r = key
 // 8(r/4) + 4g + r%4), P = exp2(S c - L2), dS = P (dP - D), dQ^T += K^T dS^T. When `masked`,
 // keys with offset above hi get P = dS = 0.
-template <int D>
-__device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D / 16],
-                                         const bf16x8 (&dof)[D / 16],
-                                         f32x16 (&dqt)[(D + 31) / 32], float c, float l2,
-                                         float nd, bool masked, int hi, int lane, int l32,
-                                         int g) {
+template <int D, bool EARLY>
+__device__ __forceinline__ void q_step(const bf16* buf, const QOps<D>& op,
+                                       const bf16x8 (&qf)[D / 16],
+                                       const bf16x8 (&dof)[D / 16],
+                                       f32x16 (&dqt)[(D + 31) / 32], float c, float l2,
+                                       float nd, bool masked, int hi, int lane, int l32,
+                                       int g) {
   using B = Bwd<D>;
-  constexpr int DS = B::DS, DB = B::DB;
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
   bf16x8 k[DS], v[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
@@ -815,8 +846,12 @@ __device__ __forceinline__ void q_update(const bf16* buf, const bf16x8 (&qf)[D /
   for (int s2 = 0; s2 < 2; ++s2) {
     const bf16x8 sf = to_bf16x8(dpt, 8 * s2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      dqt[db] = mfma32(B::MTile::tfrag(buf, 32 * db, 16 * s2, lane), sf, dqt[db]);
+    for (int db = 0; db < DB; ++db) {
+      if constexpr (EARLY)
+        dqt[db] = mfma32(op.kt[s2][db], sf, dqt[db]);
+      else
+        dqt[db] = mfma32(B::MTile::tfrag(buf, 32 * db, 16 * s2, lane), sf, dqt[db]);
+    }
   }
 }
 
@@ -883,12 +918,11 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
     bf16* nbuf = smem + (((mt - mt0) & 1) ^ 1) * B::KV_BUF;
     const int m0 = mt * 32;
     const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
+    KvOps<D> op;  // unused: transposed operands are read late (see KvOps)
     if (mt + 1 < nmt) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, m0 + 32, nbuf, w, lane);
-    if (active) {
-      f32x16 sp, dp;
-      kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
-      kv_update<D>(buf, sp, dp, dvt, dkt, c, CAUSAL && m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
-    }
+    if (active)
+      kv_step<D, false>(buf, op, kf, vf, dvt, dkt, c, CAUSAL && m0 < kw0 + 31,
+                        krow - m0 - 4 * g, lane, l32, g);
     wait_vmem();
     __syncthreads();
   }
@@ -931,14 +965,16 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
     bf16* nbuf = smem + ((kt & 1) ^ 1) * B::Q_BUF;
     const int n0 = kt * 32;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
+    QOps<D> op;  // unused: transposed operands are read late (see KvOps)
     if (kt + 1 < nkt) {
       B::MTile::template load<4>(Kr, n0 + 32, nbuf, w, lane);
       B::MTile::template load<4>(Vr, n0 + 32, nbuf + B::T, w, lane);
     }
     if (active)
-      q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.nd,
-                  (CAUSAL && n0 + 31 > qw0) || n0 + 32 > Nk,
-                  min(CAUSAL ? qrow - n0 - 4 * g : 1 << 30, Nk - 1 - n0 - 4 * g), lane, l32, g);
+      q_step<D, false>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd,
+                       (CAUSAL && n0 + 31 > qw0) || n0 + 32 > Nk,
+                       min(CAUSAL ? qrow - n0 - 4 * g : 1 << 30, Nk - 1 - n0 - 4 * g), lane,
+                       l32, g);
     wait_vmem();
     __syncthreads();
   }
@@ -1046,12 +1082,12 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
       const int m0 = 32 * mt_of(n);
       const int kw0 = 64 * kt + 32 * wp;
       const bool active = m0 + 31 >= kw0;
+      KvOps<D> op;
+      if (active) op.read(buf, lane);
       if (n + 1 < nsteps) kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n + 1), nbuf, wp, lane);
-      if (active) {
-        f32x16 sp, dp;
-        kv_scores_mfma<D>(buf, kf, vf, sp, dp, l32, g);
-        kv_update<D>(buf, sp, dp, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g, lane, g);
-      }
+      if (active)
+        kv_step<D, true>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g, lane,
+                         l32, g);
       if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
         store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
         store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
@@ -1120,13 +1156,15 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
       const int n0 = 32 * kt_of(n);
       const int qw0 = 64 * qt + 32 * wp;
       const bool active = n0 <= qw0 + 31;
+      QOps<D> op;
+      if (active) op.read(buf, lane);
       if (n + 1 < nsteps) {
         B::MTile::template load<2>(Kr, 32 * kt_of(n + 1), nbuf, wp, lane);
         B::MTile::template load<2>(Vr, 32 * kt_of(n + 1), nbuf + B::T, wp, lane);
       }
       if (active)
-        q_update<D>(buf, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
-                    qrow - n0 - 4 * g, lane, l32, g);
+        q_step<D, true>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
+                        qrow - n0 - 4 * g, lane, l32, g);
       if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
         store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
 #pragma unroll
