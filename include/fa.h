@@ -133,6 +133,32 @@ FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, i
                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * fa_backward_preprocess -- the backward's preprocessing step on its own: for every query
+ * row, L_i log2(e) and -D_i with D_i = sum_k dO_ik O_ik (problem flash_backward), written
+ * to `workspace` for fa_backward_main. fa_backward is this call followed by
+ * fa_backward_main on the same stream; callers that want to place or time the two steps
+ * separately can make the two calls themselves. Arguments mean what they mean for
+ * fa_backward. For fp32, and when B*H*Nq == 0, there is nothing to precompute and the call
+ * returns FA_SUCCESS without enqueuing anything.
+ */
+FA_API fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                 int64_t d, const void* O, const float* L, const void* dO,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_backward_main -- everything fa_backward does after fa_backward_preprocess: dQ, dK and
+ * dV from Q, K, V, dO and the per-row terms that fa_backward_preprocess left in
+ * `workspace` (which must be that call's workspace, unmodified, on the same stream or
+ * otherwise ordered after it). Arguments and errors as for fa_backward; O and L are
+ * validated as there and read only by the fp32 path.
+ */
+FA_API fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                           int64_t d, const void* Q, const void* K, const void* V,
+                           const void* O, const float* L, const void* dO, int is_causal,
+                           float scale, void* dQ, void* dK, void* dV, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* fa_status_string -- static, NUL-terminated name of a status code (never NULL). */
 FA_API const char* fa_status_string(fa_status status);
 

@@ -27,8 +27,9 @@ def declared_symbols():
     return sorted(set(re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
-    assert declared_symbols() == ["fa_backward", "fa_backward_workspace_bytes", "fa_forward",
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == ["fa_backward", "fa_backward_main", "fa_backward_preprocess",
+                                  "fa_backward_workspace_bytes", "fa_forward",
                                   "fa_status_string"]
 
 
@@ -115,6 +116,42 @@ def test_forward_empty_is_a_noop(lib, kw):
 ])
 def test_backward_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 2), (dict(d=24), 2), (dict(Nk=0), 1), (dict(q=None), 1), (dict(dk=BAD), 1),
+    (dict(ws_bytes=128 * 8 - 1), 1), (dict(ws=None), 1), (dict(scale=math.nan), 1),
+])
+def test_backward_main_rejects_like_backward(lib, kw, code):
+    args = dict(dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
+                causal=1, scale=0.125, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    assert lib.fa_backward_main(a["dtype"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["q"],
+                                a["k"], a["v"], a["o"], a["lse"], a["do"], a["causal"],
+                                a["scale"], a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"],
+                                None) == code
+
+
+def prep(lib, dtype=1, B=1, H=1, Nq=128, d=64, o=P, lse=P, do=P, ws=P, ws_bytes=1 << 30):
+    return lib.fa_backward_preprocess(dtype, B, H, Nq, d, o, lse, do, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 2), (dict(d=24), 2), (dict(Nq=-1), 1), (dict(Nq=(1 << 22) + 1), 2),
+    (dict(o=None), 1), (dict(o=BAD), 1), (dict(do=None), 1), (dict(lse=None), 1),
+    (dict(lse=P + 2), 1), (dict(ws=None), 1), (dict(ws=P + 2), 1),
+    (dict(ws_bytes=128 * 8 - 1), 1),
+])
+def test_backward_preprocess_rejects(lib, kw, code):
+    assert prep(lib, **kw) == code
+
+
+def test_backward_preprocess_noops(lib):
+    # fp32 has no preprocessing step, and there is nothing to do without query rows.
+    assert prep(lib, dtype=0, o=None, lse=None, do=None, ws=None, ws_bytes=0) == 0
+    assert prep(lib, B=0, o=None, lse=None, do=None, ws=None, ws_bytes=0) == 0
+    assert prep(lib, Nq=0, o=None, lse=None, do=None, ws=None, ws_bytes=0) == 0
 
 
 def test_backward_empty_is_a_noop(lib):

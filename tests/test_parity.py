@@ -270,3 +270,27 @@ def test_paired_and_plain_forward_agree(gpu):
         assert torch.allclose(l1[0, 0], l2[0, h], atol=1e-5, rtol=0)
         a, b = o1[0, 0].float(), o2[0, h].float()
         assert torch.all((a - b).abs() <= 2 ** -7 * a.abs().clamp(min=1.0))
+
+
+@pytest.mark.parametrize("case", [(1, 2, 256, 256, 64, "bf16", True),
+                                  (2, 1, 200, 120, 32, "bf16", False),
+                                  (1, 1, 96, 96, 16, "f32", True)],
+                         ids=lambda c: "B{}H{}q{}k{}d{}-{}-{}".format(*c))
+def test_preprocess_then_main_equals_backward(gpu, case):
+    # fa_backward is fa_backward_preprocess followed by fa_backward_main: same bits.
+    from tiled_attention_causal_amd import (backward_workspace_bytes, fa_backward,
+                                            fa_backward_main, fa_backward_preprocess,
+                                            fa_forward)
+    B, H, Nq, Nk, d, dtype, causal = case
+    note(f"case {case}")
+    inp = make_inputs(B, H, Nq, Nk, d, dtype, index=95)
+    q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, causal)
+    want = fa_backward(q, k, v, o, lse, do, causal)
+    ws = torch.full((max(4, backward_workspace_bytes(q, k)),), 255, dtype=torch.uint8,
+                    device=gpu)
+    fa_backward_preprocess(o, lse, do, ws)
+    got = fa_backward_main(q, k, v, o, lse, do, causal, None, ws)
+    torch.cuda.synchronize(gpu)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, want):
+        assert torch.equal(a, b), name

@@ -4,7 +4,8 @@
 """
 from ._lib import FAError, LIB_PATH, load  # noqa: F401
 from .ops import (FlashAttention, backward_workspace_bytes, default_scale,  # noqa: F401
-                  fa_backward, fa_forward)
+                  fa_backward, fa_backward_main, fa_backward_preprocess, fa_forward)
 
-__all__ = ["fa_forward", "fa_backward", "backward_workspace_bytes", "FlashAttention",
-           "default_scale", "FAError", "load", "LIB_PATH"]
+__all__ = ["fa_forward", "fa_backward", "fa_backward_preprocess", "fa_backward_main",
+           "backward_workspace_bytes", "FlashAttention", "default_scale", "FAError", "load",
+           "LIB_PATH"]

@@ -29,6 +29,11 @@ SIGNATURES = {
     "fa_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                    _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float, _ptr, _ptr,
                                    _ptr, _ptr, ctypes.c_size_t, _ptr]),
+    "fa_backward_preprocess": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr,
+                                              _ptr, _ptr, ctypes.c_size_t, _ptr]),
+    "fa_backward_main": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr,
+                                        _ptr, _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float,
+                                        _ptr, _ptr, _ptr, _ptr, ctypes.c_size_t, _ptr]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

@@ -90,37 +90,86 @@ fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
 }
 
-fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                      const void* Q, const void* K, const void* V, const void* O,
-                      const float* L, const void* dO, int is_causal, float scale, void* dQ,
-                      void* dK, void* dV, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  fa::Shape s;
-  const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
+// Validation shared by fa_backward and fa_backward_main (which read the same arguments).
+static fa_status check_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                int64_t d, const void* Q, const void* K, const void* V,
+                                const void* O, const float* L, const void* dO, int is_causal,
+                                float scale, void* dQ, void* dK, void* dV, void* workspace,
+                                size_t workspace_bytes, fa::Shape* s, bool* nothing) {
+  const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, s);
   if (st != FA_SUCCESS) return st;
   const size_t ws_need = fa_backward_workspace_bytes(dtype, B, H, Nq, Nk, d);
   if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
   if (ws_need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
     return FA_ERROR_INVALID_VALUE;
-  const bool has_q = (int64_t)s.BH * Nq > 0, has_k = (int64_t)s.BH * Nk > 0;
-  if (!has_q && !has_k) return FA_SUCCESS;
+  const bool has_q = (int64_t)s->BH * Nq > 0, has_k = (int64_t)s->BH * Nk > 0;
+  *nothing = !has_q && !has_k;
+  if (*nothing) return FA_SUCCESS;
   if (has_q && Nk == 0) return FA_ERROR_INVALID_VALUE;  // softmax over no keys
   if (has_q && (bad_ptr(Q) || bad_ptr(O) || bad_ptr(dO) || bad_ptr(dQ) || L == nullptr ||
                 (reinterpret_cast<uintptr_t>(L) & 3u) != 0))
     return FA_ERROR_INVALID_VALUE;
   if (has_k && (bad_ptr(K) || bad_ptr(V) || bad_ptr(dK) || bad_ptr(dV)))
     return FA_ERROR_INVALID_VALUE;
+  return FA_SUCCESS;
+}
+
+fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                 const void* O, const float* L, const void* dO,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  fa::Shape s;
+  // Keys play no part here; Nk = 0 keeps the size checks to the query side.
+  const fa_status st = check_common(dtype, B, H, Nq, 0, d, 1.f, 0, &s);
+  if (st != FA_SUCCESS) return st;
+  const size_t ws_need = fa_backward_workspace_bytes(dtype, B, H, Nq, 0, d);
+  if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
+  if (ws_need == 0) return FA_SUCCESS;  // fp32, or no query rows: nothing to precompute
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
+      bad_ptr(O) || bad_ptr(dO) || L == nullptr || (reinterpret_cast<uintptr_t>(L) & 3u) != 0)
+    return FA_ERROR_INVALID_VALUE;
+  const hipError_t e = fa::launch_bwd_prep_bf16(s, O, L, dO, static_cast<float*>(workspace),
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
+fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                           int64_t d, const void* Q, const void* K, const void* V,
+                           const void* O, const float* L, const void* dO, int is_causal,
+                           float scale, void* dQ, void* dK, void* dV, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  fa::Shape s;
+  bool nothing = false;
+  const fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal,
+                                      scale, dQ, dK, dV, workspace, workspace_bytes, &s,
+                                      &nothing);
+  if (st != FA_SUCCESS || nothing) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
-    e = fa::launch_bwd_bf16(s, Q, K, V, O, L, dO, dQ, dK, dV, static_cast<float*>(workspace),
-                            hs);
+    e = fa::launch_bwd_main_bf16(s, Q, K, V, dO, dQ, dK, dV,
+                                 static_cast<const float*>(workspace), hs);
   else
     e = fa::launch_bwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
                            static_cast<const float*>(V), static_cast<const float*>(O), L,
                            static_cast<const float*>(dO), static_cast<float*>(dQ),
                            static_cast<float*>(dK), static_cast<float*>(dV), hs);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
+fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      const void* Q, const void* K, const void* V, const void* O,
+                      const float* L, const void* dO, int is_causal, float scale, void* dQ,
+                      void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  fa::Shape s;
+  bool nothing = false;
+  fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale,
+                                dQ, dK, dV, workspace, workspace_bytes, &s, &nothing);
+  if (st != FA_SUCCESS || nothing) return st;
+  st = fa_backward_preprocess(dtype, B, H, Nq, d, O, L, dO, workspace, workspace_bytes, stream);
+  if (st != FA_SUCCESS) return st;
+  return fa_backward_main(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale, dQ, dK,
+                          dV, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

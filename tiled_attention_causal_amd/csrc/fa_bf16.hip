@@ -758,6 +758,9 @@ __device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
 #pragma unroll
     for (int i = 0; i < 4; ++i) dp[4 * j + i] = n4[i];
   }
+  // With registers to spare (EARLY), all of these reads are issued before the first MFMA,
+  // so the score MFMAs wait for one LDS round trip rather than one per operand pair.
+  if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     sp = mfma32(qa[s], kf[s], sp);
@@ -828,6 +831,7 @@ __device__ __forceinline__ void q_step(const bf16* buf, const QOps<D>& op,
     k[s] = B::MTile::frag(buf, l32, 2 * s + g);
     v[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
+  if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);  // as in kv_step
   f32x16 st[1] = {zero16()}, dpt;
 #pragma unroll
   for (int r = 0; r < 16; ++r) dpt[r] = nd;  // dP starts at -D of this lane's query
@@ -1227,21 +1231,25 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* O,
-                 const float* L, const void* dO, void* dQ, void* dK, void* dV, float* ws,
-                 hipStream_t stream) {
-  // Workspace: L2 for the B*H*Nq rows, then ND for the same rows.
+// Workspace layout shared by the two backward launches: L2 for the B*H*Nq query rows, then
+// ND for the same rows.
+template <int D>
+hipError_t bwd_prep_t(const Shape& s, const void* O, const float* L, const void* dO, float* ws,
+                      hipStream_t stream) {
   const long long rows = (long long)s.BH * s.Nq;
-  float* L2 = ws;
-  float* ND = ws + rows;
-  if (rows > 0) {
-    const long long prep_grid = std::min((rows * (D / 8) + 255) / 256, 1LL << 16);
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_grid), dim3(256), 0, stream,
-                       (const bf16*)O, (const bf16*)dO, L, L2, ND, rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (rows == 0) return hipSuccess;
+  const long long grid = std::min((rows * (D / 8) + 255) / 256, 1LL << 16);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const bf16*)O, (const bf16*)dO, L, ws, ws + rows, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                 void* dQ, void* dK, void* dV, const float* ws, hipStream_t stream) {
+  const long long rows = (long long)s.BH * s.Nq;
+  const float* L2 = ws;
+  const float* ND = ws + rows;
   // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
   // the longest tile on the critical path of a small grid; see bwd_causal_paired_kernel.
   // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
@@ -1282,13 +1290,29 @@ hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const v
 #undef FA_FWD
 }
 
-hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                           const void* O, const float* L, const void* dO, void* dQ, void* dK,
-                           void* dV, float* workspace, hipStream_t stream) {
-#define FA_BWD(DD)                                                                            \
-  case DD:                                                                                    \
-    return s.causal ? bwd_t<DD, true>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace, stream)    \
-                    : bwd_t<DD, false>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace, stream);
+hipError_t launch_bwd_prep_bf16(const Shape& s, const void* O, const float* L, const void* dO,
+                                float* workspace, hipStream_t stream) {
+  switch (s.d) {
+    case 16:
+      return bwd_prep_t<16>(s, O, L, dO, workspace, stream);
+    case 32:
+      return bwd_prep_t<32>(s, O, L, dO, workspace, stream);
+    case 64:
+      return bwd_prep_t<64>(s, O, L, dO, workspace, stream);
+    case 128:
+      return bwd_prep_t<128>(s, O, L, dO, workspace, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                                const void* dO, void* dQ, void* dK, void* dV,
+                                const float* workspace, hipStream_t stream) {
+#define FA_BWD(DD)                                                                          \
+  case DD:                                                                                  \
+    return s.causal ? bwd_t<DD, true>(s, Q, K, V, dO, dQ, dK, dV, workspace, stream)        \
+                    : bwd_t<DD, false>(s, Q, K, V, dO, dQ, dK, dV, workspace, stream);
   switch (s.d) {
     FA_BWD(16)
     FA_BWD(32)

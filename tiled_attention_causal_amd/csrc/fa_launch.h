@@ -17,11 +17,13 @@ struct Shape {
 
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V, void* O,
                            float* L, hipStream_t stream);
-// `workspace` holds 2 * BH * Nq floats: per-row terms written by the first of the two kernels
-// this launches and read by the second.
-hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                           const void* O, const float* L, const void* dO, void* dQ, void* dK,
-                           void* dV, float* workspace, hipStream_t stream);
+// The bf16 backward is two launches sharing `workspace` (2 * BH * Nq floats): the first writes
+// per-row terms (L log2(e) and -D) from O, L and dO, the second reads them.
+hipError_t launch_bwd_prep_bf16(const Shape& s, const void* O, const float* L, const void* dO,
+                                float* workspace, hipStream_t stream);
+hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                                const void* dO, void* dQ, void* dK, void* dV,
+                                const float* workspace, hipStream_t stream);
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           float* O, float* L, hipStream_t stream);
 hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const float* V,

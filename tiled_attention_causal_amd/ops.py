@@ -71,15 +71,8 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: boo
     return out, lse
 
 
-def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-                lse: torch.Tensor, do: torch.Tensor, is_causal: bool = False,
-                scale: float | None = None, dq: torch.Tensor | None = None,
-                dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None):
-    """dQ, dK, dV of the attention forward, from Q, K, V, O, L and dO.
-
-    `workspace`, if given, is a device tensor of at least backward_workspace_bytes() bytes
-    that the call may overwrite; otherwise one is allocated."""
+def _backward_args(q, k, v, o, lse, do, dq, dk, dv, workspace):
+    """Checked tensors and sizes shared by the backward entry points."""
     lib = _lib.load()
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -101,12 +94,59 @@ def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
         ws, ws_bytes = workspace, workspace.nbytes
     else:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    return lib, (B, H, Nq, Nk, d), dq, dk, dv, ws, ws_bytes
+
+
+def fa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                lse: torch.Tensor, do: torch.Tensor, is_causal: bool = False,
+                scale: float | None = None, dq: torch.Tensor | None = None,
+                dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """dQ, dK, dV of the attention forward, from Q, K, V, O, L and dO.
+
+    `workspace`, if given, is a device tensor of at least backward_workspace_bytes() bytes
+    that the call may overwrite; otherwise one is allocated."""
+    lib, (B, H, Nq, Nk, d), dq, dk, dv, ws, ws_bytes = _backward_args(
+        q, k, v, o, lse, do, dq, dk, dv, workspace)
     sc = default_scale(d) if scale is None else float(scale)
-    st = lib.fa_backward(_DTYPES[dt], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                         o.data_ptr(), lse.data_ptr(), do.data_ptr(), int(bool(is_causal)), sc,
-                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+    st = lib.fa_backward(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
+                         v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                         int(bool(is_causal)), sc, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q))
     _raise(st, "fa_backward")
+    return dq, dk, dv
+
+
+def fa_backward_preprocess(o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor,
+                           workspace: torch.Tensor):
+    """The backward's preprocessing step alone: per-row L log2(e) and -D into `workspace`."""
+    lib = _lib.load()
+    B, H, Nq, d = o.shape
+    if o.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {o.dtype}")
+    _check("do", do, (B, H, Nq, d), o.dtype, o.device)
+    _check("lse", lse, (B, H, Nq), torch.float32, o.device)
+    if workspace.device != o.device:
+        raise ValueError(f"workspace must be on {o.device}")
+    st = lib.fa_backward_preprocess(_DTYPES[o.dtype], B, H, Nq, d, o.data_ptr(), lse.data_ptr(),
+                                    do.data_ptr(), workspace.data_ptr(), workspace.nbytes,
+                                    _stream_ptr(o))
+    _raise(st, "fa_backward_preprocess")
+
+
+def fa_backward_main(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, do: torch.Tensor, is_causal: bool, scale: float | None,
+                     workspace: torch.Tensor, dq: torch.Tensor | None = None,
+                     dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Everything fa_backward does after fa_backward_preprocess filled `workspace`."""
+    lib, (B, H, Nq, Nk, d), dq, dk, dv, ws, ws_bytes = _backward_args(
+        q, k, v, o, lse, do, dq, dk, dv, workspace)
+    sc = default_scale(d) if scale is None else float(scale)
+    st = lib.fa_backward_main(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                              int(bool(is_causal)), sc, dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), ws.data_ptr(), ws_bytes, _stream_ptr(q))
+    _raise(st, "fa_backward_main")
     return dq, dk, dv
 
 
