@@ -1020,6 +1020,39 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
   }
 }
 
+// Runs step(n, cur) for n = 0 .. nsteps-1 over tiles that fetch(n, dst) loads straight into
+// LDS, two tiles ahead, through three buffers. Each step issues the loads of tile n+2, runs,
+// then waits for tile n+1 only (vmcnt(KEEP), KEEP = vector-memory instructions one fetch
+// issues per wave) and meets the other waves at an LDS-only barrier. The loop sits in one
+// function whose buffers are restrict parameters and is unrolled by three, so every access
+// names its buffer statically: the compiler can then tell that a step's (transposed) LDS
+// reads of `cur` do not alias the loads in flight into the other two buffers, and inserts no
+// wait for them. A step that issues other vector-memory instructions must wait for all of
+// them itself before returning.
+template <int KEEP, class Fetch, class Step>
+__device__ __forceinline__ void stream3(int nsteps, bf16* __restrict__ b0, bf16* __restrict__ b1,
+                                        bf16* __restrict__ b2, Fetch&& fetch, Step&& step) {
+  if (nsteps > 0) fetch(0, b0);
+  if (nsteps > 1) fetch(1, b1);
+  wait_vmem();
+  __syncthreads();
+  auto one = [&](int n, bf16* cur, bf16* pre) {
+    const bool more = n + 2 < nsteps;
+    if (more) fetch(n + 2, pre);
+    step(n, cur);
+    if (more)
+      wait_vmem_keep<KEEP>();
+    else
+      wait_vmem();
+    lds_barrier();
+  };
+  for (int n = 0; n < nsteps; n += 3) {
+    one(n, b0, b2);
+    if (n + 1 < nsteps) one(n + 1, b1, b0);
+    if (n + 2 < nsteps) one(n + 2, b2, b1);
+  }
+}
+
 // Causal backward with complementary tile pairing, for Nq = Nk = N, N % 128 == 0 (the
 // counterpart of fwd_causal_paired_kernel). Tiles are 64 rows, held by a wave pair (32 rows
 // per wave); steps are 32-row moving tiles. Per head, T/2 workgroups do dK/dV and T/2 do dQ
@@ -1040,7 +1073,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
   using B = Bwd<D>;
   constexpr int DS = B::DS, DB = B::DB;
   constexpr int SM = B::KV_BUF > B::Q_BUF ? B::KV_BUF : B::Q_BUF;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2][2][SM];  // [pair][buffer]
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2][3][SM];  // [pair][buffer]
+  static_assert(B::MTile::NKIB % 2 == 0, "each wave of a pair loads the same number of blocks");
 
   const int T = N / 64, half = T / 2;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -1077,36 +1111,33 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
       dvt[db] = zero16();
       dkt[db] = zero16();
     }
-    kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(0), smem[pr][0], wp, lane);
-    wait_vmem();
-    __syncthreads();
-    for (int n = 0; n < nsteps; ++n) {
-      bf16* buf = smem[pr][n & 1];
-      bf16* nbuf = smem[pr][(n & 1) ^ 1];
-      const int m0 = 32 * mt_of(n);
-      const int kw0 = 64 * kt + 32 * wp;
-      const bool active = m0 + 31 >= kw0;
-      KvOps<D> op;
-      if (active) op.read(buf, lane);
-      if (n + 1 < nsteps) kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n + 1), nbuf, wp, lane);
-      if (active)
-        kv_step<D, true>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g, lane,
-                         l32, g);
-      if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
-        store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
-        store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+    // Per wave, one fetch issues NKIB/2 loads for each of Q and dO, and one for L2 or ND.
+    constexpr int kKeep = B::MTile::NKIB + 1;
+    stream3<kKeep>(
+        nsteps, smem[pr][0], smem[pr][1], smem[pr][2],
+        [&](int n, bf16* dst) { kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n), dst, wp, lane); },
+        [&](int n, bf16* buf) {
+          const int m0 = 32 * mt_of(n);
+          const int kw0 = 64 * kt + 32 * wp;
+          if (m0 + 31 >= kw0) {
+            KvOps<D> op;
+            op.read(buf, lane);
+            kv_step<D, true>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g,
+                             lane, l32, g);
+          }
+          if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
+            store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
+            store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dvt[db] = zero16();
-          dkt[db] = zero16();
-        }
-        kt = tA;
-        krow = 64 * kt + 32 * wp + l32;
-        load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
-      }
-      wait_vmem();
-      __syncthreads();
-    }
+            for (int db = 0; db < DB; ++db) {
+              dvt[db] = zero16();
+              dkt[db] = zero16();
+            }
+            kt = tA;
+            krow = 64 * kt + 32 * wp + l32;
+            load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);  // waits for all its loads
+          }
+        });
     // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end).
     const bool p1_has_A = nsteps > nB;
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
@@ -1150,36 +1181,32 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     f32x16 dqt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = zero16();
-    B::MTile::template load<2>(Kr, 32 * kt_of(0), smem[pr][0], wp, lane);
-    B::MTile::template load<2>(Vr, 32 * kt_of(0), smem[pr][0] + B::T, wp, lane);
-    wait_vmem();
-    __syncthreads();
-    for (int n = 0; n < nsteps; ++n) {
-      const bf16* buf = smem[pr][n & 1];
-      bf16* nbuf = smem[pr][(n & 1) ^ 1];
-      const int n0 = 32 * kt_of(n);
-      const int qw0 = 64 * qt + 32 * wp;
-      const bool active = n0 <= qw0 + 31;
-      QOps<D> op;
-      if (active) op.read(buf, lane);
-      if (n + 1 < nsteps) {
-        B::MTile::template load<2>(Kr, 32 * kt_of(n + 1), nbuf, wp, lane);
-        B::MTile::template load<2>(Vr, 32 * kt_of(n + 1), nbuf + B::T, wp, lane);
-      }
-      if (active)
-        q_step<D, true>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
-                        qrow - n0 - 4 * g, lane, l32, g);
-      if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
-        store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
+    // Per wave, one fetch issues NKIB/2 loads for each of K and V.
+    constexpr int kKeep = B::MTile::NKIB;
+    stream3<kKeep>(
+        nsteps, smem[pr][0], smem[pr][1], smem[pr][2],
+        [&](int n, bf16* dst) {
+          B::MTile::template load<2>(Kr, 32 * kt_of(n), dst, wp, lane);
+          B::MTile::template load<2>(Vr, 32 * kt_of(n), dst + B::T, wp, lane);
+        },
+        [&](int n, bf16* buf) {
+          const int n0 = 32 * kt_of(n);
+          const int qw0 = 64 * qt + 32 * wp;
+          if (n0 <= qw0 + 31) {
+            QOps<D> op;
+            op.read(buf, lane);
+            q_step<D, true>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
+                            qrow - n0 - 4 * g, lane, l32, g);
+          }
+          if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
+            store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) dqt[db] = zero16();
-        qt = tA;
-        qrow = 64 * qt + 32 * wp + l32;
-        row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
-      }
-      wait_vmem();
-      __syncthreads();
-    }
+            for (int db = 0; db < DB; ++db) dqt[db] = zero16();
+            qt = tA;
+            qrow = 64 * qt + 32 * wp + l32;
+            row.load(Qr, dOr, L2r, NDr, qrow, g, neg);  // waits for all its loads
+          }
+        });
     const bool p1_has_A = nsteps > nB;
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
     if (pr == 1 && p1_has_A) {

@@ -44,6 +44,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // Wait until every outstanding vector-memory load of this wave has returned.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most K vector-memory instructions of this wave are outstanding (vmcnt(K)):
+// they return in issue order, so this waits for everything but the K most recent.
+template <int K>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(K >= 0 && K < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | K);
+}
+
+// Workgroup barrier that publishes this wave's LDS writes and completes its LDS reads
+// (lgkmcnt(0)) but leaves its outstanding vector-memory loads, including loads into LDS, in
+// flight; __syncthreads() would wait for those too. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16) on the matrix cores.
 // Fragment layout with g = lane / 32:
 //   A: lane holds row (lane % 32), k = 8g .. 8g+7;  B: lane holds column (lane % 32), same k;
