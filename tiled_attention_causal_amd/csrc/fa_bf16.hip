@@ -439,27 +439,29 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   const bool p1_has_A = T - tB > s;
   constexpr int XS = 16 * DB + 2;  // per lane: O block(s), m, l
   static_assert(2 * 64 * XS * sizeof(float) <= sizeof(sb0), "merge area must fit in sb0");
-  float* xf = reinterpret_cast<float*>(&sb0[0][0][0]);  // 2 waves x 64 lanes x XS
+  // Component-major merge record (component k of wave wp's lane at k * 128 + wp * 64 + lane):
+  // consecutive lanes write consecutive words, so the exchange is free of bank conflicts.
+  float* xf = reinterpret_cast<float*>(&sb0[0][0][0]);
   if (pr == 1 && p1_has_A) {
-    float* x = xf + (wp * 64 + lane) * XS;
+    float* x = xf + wp * 64 + lane;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[16 * db + r] = o[db][r];
-    x[16 * DB] = m;
-    x[16 * DB + 1] = l;
+      for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[db][r];
+    x[16 * DB * 128] = m;
+    x[(16 * DB + 1) * 128] = l;
   }
   __syncthreads();
   if (pr == 0) {
     if (p1_has_A) {
-      const float* x = xf + (wp * 64 + lane) * XS;
-      const float m1 = x[16 * DB], l1 = x[16 * DB + 1];
+      const float* x = xf + wp * 64 + lane;
+      const float m1 = x[16 * DB * 128], l1 = x[(16 * DB + 1) * 128];
       const float mm = fmaxf(m, m1);
       const float a0 = fast_exp2((m - mm) * c), a1 = fast_exp2((m1 - mm) * c);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + x[16 * db + r] * a1;
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + x[(16 * db + r) * 128] * a1;
       l = l * a0 + l1 * a1;
       m = mm;
     }
@@ -1138,30 +1140,32 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
             load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);  // waits for all its loads
           }
         });
-    // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end).
+    // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end). The
+    // merge record is component-major (component k of wave wp's lane at k * 128 + wp * 64 +
+    // lane), so the exchange is free of bank conflicts.
     const bool p1_has_A = nsteps > nB;
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
     static_assert(2 * 64 * XS * sizeof(float) <= sizeof(smem), "merge area must fit");
     if (pr == 1 && p1_has_A) {
-      float* x = xf + (wp * 64 + lane) * XS;
+      float* x = xf + wp * 64 + lane;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          x[16 * db + r] = dkt[db][r];
-          x[16 * (DB + db) + r] = dvt[db][r];
+          x[(16 * db + r) * 128] = dkt[db][r];
+          x[(16 * (DB + db) + r) * 128] = dvt[db][r];
         }
     }
     __syncthreads();
     if (pr == 0) {
       if (p1_has_A) {
-        const float* x = xf + (wp * 64 + lane) * XS;
+        const float* x = xf + wp * 64 + lane;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            dkt[db][r] += x[16 * db + r];
-            dvt[db][r] += x[16 * (DB + db) + r];
+            dkt[db][r] += x[(16 * db + r) * 128];
+            dvt[db][r] += x[(16 * (DB + db) + r) * 128];
           }
       }
       store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
@@ -1210,20 +1214,20 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     const bool p1_has_A = nsteps > nB;
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
     if (pr == 1 && p1_has_A) {
-      float* x = xf + (wp * 64 + lane) * XS;
+      float* x = xf + wp * 64 + lane;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[16 * db + r] = dqt[db][r];
+        for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = dqt[db][r];
     }
     __syncthreads();
     if (pr == 0) {
       if (p1_has_A) {
-        const float* x = xf + (wp * 64 + lane) * XS;
+        const float* x = xf + wp * 64 + lane;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dqt[db][r] += x[16 * db + r];
+          for (int r = 0; r < 16; ++r) dqt[db][r] += x[(16 * db + r) * 128];
       }
       store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
     }

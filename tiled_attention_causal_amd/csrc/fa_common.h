@@ -106,15 +106,22 @@ __device__ __forceinline__ int chunk_row(int kc, int e) {
   return 16 * (kc >> 1) + 8 * (e >> 2) + 4 * (kc & 1) + (e & 3);
 }
 
-// XOR key of row r for an LDS tile with NCH 16-byte chunks per row. With 8 or more chunks
-// the key is 2(r%4) ^ ((r/4)%2): eight consecutive rows reading one chunk (an MFMA row
-// fragment) get eight distinct keys, and four consecutive rows reading a pair of adjacent
-// chunks (a transposed fragment, ds_read_b64_tr_b16) get four disjoint chunk pairs, so
-// neither pattern repeats an LDS bank. Narrower tiles use (r ^ r/8) % NCH.
+// XOR key of row r for an LDS tile with NCH 16-byte chunks per row. With 8 chunks (64
+// columns) the key is 2(r%4) ^ ((r/4)%2) ^ 2((r/8)%2). The first two terms give four
+// consecutive rows that read a pair of adjacent chunks (a transposed fragment,
+// ds_read_b64_tr_b16) four disjoint chunk pairs; the last term separates rows r and r+8,
+// which a 16-byte row-fragment read (ds_read_b128) otherwise puts on the same banks. With 16
+// chunks (128 columns) the key also moves odd rows to the other half of the row: 8(r%2).
+// Both were chosen by measurement on gfx950 (SQ_LDS_BANK_CONFLICT, both access patterns as
+// the kernels issue them): no conflicts, where the obvious keys leave one pattern at 50%.
+// Narrower tiles use (r ^ r/8) % NCH.
 template <int NCH>
 __device__ __forceinline__ int swz_key(int r) {
-  if constexpr (NCH >= 8)
-    return ((r & 3) << 1) ^ ((r >> 2) & 1);
+  const int k8 = ((r & 3) << 1) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+  if constexpr (NCH >= 16)
+    return k8 ^ ((r & 1) << 3);
+  else if constexpr (NCH == 8)
+    return k8;
   else
     return (r ^ (r >> 3)) & (NCH - 1);
 }
