@@ -7,9 +7,12 @@ in HBM before the timed region starts. Counted work (the metric's convention): f
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Prints one JSON line. Extra modes for profiling runs:
+Prints one JSON line. Extra modes:
     --copy-calibration   run only a plain device copy of known size (HBM counter scaling)
     --all                also print a per-workload table to stderr
+    --sweep              forward / backward / end-to-end latency of these kernels against
+                         plain PyTorch attention over sequence length x head dim x dtype
+                         (a markdown table on stdout, no JSON line)
 """
 from __future__ import annotations
 
@@ -41,6 +44,16 @@ def parse():
                     help="run the oracle sample for at least this much CPU time")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-n", default="128,256,512,1024,2048,4096,8192")
+    ap.add_argument("--sweep-d", default="16,32,64,128")
+    ap.add_argument("--sweep-dtypes", default="bf16,f32")
+    ap.add_argument("--sweep-batch", type=int, default=1)
+    ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--sweep-flash-only", action="store_true",
+                    help="time only the flash kernels (e.g. past plain attention's memory)")
+    ap.add_argument("--sweep-plain-only", action="store_true",
+                    help="time only plain attention (e.g. to find where it runs out of memory)")
     return ap.parse_args()
 
 
@@ -196,6 +209,136 @@ def cpu_baseline(w, min_s, budget_s):
                       f"counted FLOPs as on the GPU"}
 
 
+def plain_attention_forward(q, k, v, causal, scale, mask):
+    """Attention as separate PyTorch operations, the baseline of "Systems and Parallelism"
+    (CS336 field map, A2), problem pytorch_attention: S = Q K^T * scale, causal mask,
+    softmax over the keys, O = P V. The N x N matrix P is kept for the backward."""
+    import torch
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    del s
+    return torch.matmul(p, v), p
+
+
+def plain_attention_backward(q, k, v, p, do, scale):
+    """Gradients of plain_attention_forward's graph, written out as autograd forms them
+    (softmax backward dS = P (dP - rowsum(dP P))), with every transposed operand made
+    contiguous before its batched product."""
+    import torch
+    dv = torch.matmul(p.transpose(-1, -2).contiguous(), do)
+    dp = torch.matmul(do, v.transpose(-1, -2).contiguous())
+    ds = p * (dp - (dp * p).sum(-1, keepdim=True))
+    del dp
+    dq = torch.matmul(ds, k) * scale
+    dk = torch.matmul(ds.transpose(-1, -2).contiguous(), q) * scale
+    return dq, dk, dv
+
+
+def bench_ms(fn, reps, flush):
+    """Median event time of fn() over `reps` runs after three warm-up runs, with the caches
+    flushed (a 512 MiB fill) before every run, as triton.testing.do_bench does."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def sweep(args):
+    """The flash_benchmarking comparison: these kernels against plain PyTorch attention,
+    causal, batch `--sweep-batch`, one head, over sequence length x head dim x dtype.
+    Latencies are medians in ms; plain attention that runs out of memory is reported as
+    OOM, with its memory in use before the backward where it ran."""
+    import torch
+    from seeded_inputs import make_inputs
+    from tiled_attention_causal_amd import backward_workspace_bytes, fa_backward, fa_forward
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.int8, device=dev)
+    B = args.sweep_batch
+    ns = [int(x) for x in args.sweep_n.split(",")]
+    ds = [int(x) for x in args.sweep_d.split(",")]
+    print(f"| dtype | N | d | flash fwd | flash bwd | flash fwd+bwd | plain fwd | plain bwd "
+          f"| plain fwd+bwd | fwd+bwd speed-up | plain memory before bwd |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for dtype in args.sweep_dtypes.split(","):
+        for n in ns:
+            mask = None
+            for d in ds:
+                inp = make_inputs(B, 1, n, n, d, dtype, index=7000 + n + d)
+                q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+                scale = 1.0 / d ** 0.5
+                row = [dtype, str(n), str(d)]
+                fa = ["-"] * 3
+                if not args.sweep_plain_only:
+                    o, lse = fa_forward(q, k, v, True, scale)
+                    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                    ws = torch.empty(max(1, backward_workspace_bytes(q, k)), dtype=torch.uint8,
+                                     device=dev)
+
+                    def fa_fwd():
+                        fa_forward(q, k, v, True, scale, out=o, lse=lse)
+
+                    def fa_bwd():
+                        fa_backward(q, k, v, o, lse, do, True, scale, dq=dq, dk=dk, dv=dv,
+                                    workspace=ws)
+
+                    def fa_e2e():
+                        fa_fwd()
+                        fa_bwd()
+
+                    fa = [bench_ms(f, args.sweep_reps, flush) for f in (fa_fwd, fa_bwd, fa_e2e)]
+                    del o, lse, dq, dk, dv, ws
+                pl = ["-"] * 3
+                mem = "-"
+                if not args.sweep_flash_only:
+                    try:
+                        if mask is None:
+                            mask = torch.ones(n, n, dtype=torch.bool, device=dev).triu_(1)
+                        state = {}
+
+                        def pl_fwd():
+                            state["o"], state["p"] = plain_attention_forward(q, k, v, True,
+                                                                             scale, mask)
+
+                        def pl_bwd():
+                            plain_attention_backward(q, k, v, state["p"], do, scale)
+
+                        def pl_e2e():
+                            pl_fwd()
+                            pl_bwd()
+
+                        pl_fwd()
+                        torch.cuda.synchronize()
+                        mem = f"{(torch.cuda.memory_allocated() - flush.numel()) / 2**20:.0f} MiB"
+                        pl = [bench_ms(f, args.sweep_reps, flush)
+                              for f in (pl_fwd, pl_bwd, pl_e2e)]
+                        state.clear()
+                    except torch.cuda.OutOfMemoryError:
+                        state.clear()
+                        pl = ["OOM"] * 3
+                        torch.cuda.empty_cache()
+                fmt = [f"{x:.4f}" if isinstance(x, float) else x for x in fa + pl]
+                spd = (f"{pl[2] / fa[2]:.1f}x" if isinstance(pl[2], float)
+                       and isinstance(fa[2], float) else "-")
+                print("| " + " | ".join(row + fmt + [spd, mem]) + " |", flush=True)
+                del q, k, v, do
+            del mask
+            torch.cuda.empty_cache()
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -226,6 +369,9 @@ def main():
         sys.exit(1)
     import tiled_attention_causal_amd
     tiled_attention_causal_amd.load()  # fail loudly if the HIP library is missing
+    if args.sweep:
+        sweep(args)
+        return
 
     w = WORKLOADS[args.workload]
     fl = w.counted_flops()
