@@ -13,6 +13,8 @@ Prints one JSON line. Extra modes:
     --sweep              forward / backward / end-to-end latency of these kernels against
                          plain PyTorch attention over sequence length x head dim x dtype
                          (a markdown table on stdout, no JSON line)
+    --e2e                training steps of a toy decoder with plain attention, then with the
+                         flash kernels monkey-patched in as its attention (two JSON lines)
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--e2e", action="store_true",
+                    help="training-step time of a toy decoder, plain vs flash attention")
     ap.add_argument("--sweep-n", default="128,256,512,1024,2048,4096,8192")
     ap.add_argument("--sweep-d", default="16,32,64,128")
     ap.add_argument("--sweep-dtypes", default="bf16,f32")
@@ -339,6 +343,122 @@ def sweep(args):
             torch.cuda.empty_cache()
 
 
+class PlainAttention:
+    """Plain attention as an autograd function (forward and backward of plain_attention_*),
+    so that a model using it never has autograd form a batched product on a transposed
+    view."""
+
+    @staticmethod
+    def apply(q, k, v, scale):
+        import torch
+
+        class _F(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v):
+                n = q.shape[-2]
+                masked = torch.ones(n, n, dtype=torch.bool, device=q.device).triu_(1)
+                o, p = plain_attention_forward(q, k, v, True, scale, masked)
+                ctx.save_for_backward(q, k, v, p)
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, p = ctx.saved_tensors
+                return plain_attention_backward(q, k, v, p, do.contiguous(), scale)
+
+        return _F.apply(q.contiguous(), k.contiguous(), v.contiguous())
+
+
+def scaled_dot_product_attention(q, k, v, mask=None, is_causal=False, scale=None):
+    """The toy model's attention function (module level, so it can be monkey-patched):
+    plain attention under a causal keep-mask."""
+    if mask is None and not is_causal:
+        raise NotImplementedError("the toy model is causal")
+    return PlainAttention.apply(q, k, v, scale if scale is not None else q.shape[-1] ** -0.5)
+
+
+def toy_model(d_model, n_heads, d_ff, n_layers, dtype, device, seed=0):
+    """A small pre-norm decoder stack (RMSNorm, causal multi-head attention, SwiGLU MLP) with
+    random weights, calling this module's scaled_dot_product_attention for attention."""
+    import torch
+
+    g = torch.Generator().manual_seed(seed)
+
+    def w(*shape):
+        return (torch.randn(*shape, generator=g) * shape[-1] ** -0.5).to(device, dtype)
+
+    class Block(torch.nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.wqkv = torch.nn.Parameter(w(3 * d_model, d_model))
+            self.wo = torch.nn.Parameter(w(d_model, d_model))
+            self.w1 = torch.nn.Parameter(w(d_ff, d_model))
+            self.w3 = torch.nn.Parameter(w(d_ff, d_model))
+            self.w2 = torch.nn.Parameter(w(d_model, d_ff))
+            self.g1 = torch.nn.Parameter(torch.ones(d_model, device=device, dtype=dtype))
+            self.g2 = torch.nn.Parameter(torch.ones(d_model, device=device, dtype=dtype))
+
+        @staticmethod
+        def rms(x, gain):
+            xf = x.float()
+            return (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + 1e-5)).to(x.dtype) * gain
+
+        def forward(self, x):
+            B, N, _ = x.shape
+            h = self.rms(x, self.g1).reshape(B * N, d_model)
+            qkv = (h @ self.wqkv.t()).view(B, N, 3, n_heads, d_model // n_heads)
+            q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+            keep = torch.ones(N, N, dtype=torch.bool, device=x.device).tril_()
+            a = sys.modules[__name__].scaled_dot_product_attention(q, k, v, keep)
+            a = a.transpose(1, 2).reshape(B * N, d_model)
+            x = x + (a @ self.wo.t()).view(B, N, d_model)
+            h = self.rms(x, self.g2).reshape(B * N, d_model)
+            f = torch.nn.functional.silu(h @ self.w1.t()) * (h @ self.w3.t())
+            return x + (f @ self.w2.t()).view(B, N, d_model)
+
+    return torch.nn.Sequential(*[Block() for _ in range(n_layers)])
+
+
+def e2e(args):
+    """Training steps of the toy decoder (forward, backward, AdamW) with plain attention and
+    then with the flash kernels patched in as its attention function."""
+    import torch
+    from tiled_attention_causal_amd import integration
+
+    dev = torch.device("cuda:0")
+    B, N, d_model, H, d_ff, L = 4, 1024, 768, 12, 2048, 4
+    model = toy_model(d_model, H, d_ff, L, torch.bfloat16, dev)
+    opt = torch.optim.AdamW(model.parameters(), lr=1e-4)
+    x = (torch.randn(B, N, d_model, generator=torch.Generator().manual_seed(1))
+         .to(dev, torch.bfloat16))
+
+    def step():
+        opt.zero_grad(set_to_none=True)
+        loss = model(x).float().pow(2).mean()
+        loss.backward()
+        opt.step()
+
+    def timed(steps):
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    mod = sys.modules[__name__]
+    t_plain = timed(args.steps)
+    with integration.patched(mod, "scaled_dot_product_attention"):
+        t_flash = timed(args.steps)
+    cfg = {"B": B, "N": N, "d_model": d_model, "heads": H, "d_ff": d_ff, "layers": L,
+           "dtype": "bf16", "causal": True}
+    for name, t in (("plain", t_plain), ("flash", t_flash)):
+        print(json.dumps({"e2e": name, "ms_per_step": round(t * 1e3, 4),
+                          "tokens_per_s": round(B * N / t, 1), "config": cfg}))
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -371,6 +491,9 @@ def main():
     tiled_attention_causal_amd.load()  # fail loudly if the HIP library is missing
     if args.sweep:
         sweep(args)
+        return
+    if args.e2e:
+        e2e(args)
         return
 
     w = WORKLOADS[args.workload]
