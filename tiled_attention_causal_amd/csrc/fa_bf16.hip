@@ -682,14 +682,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
     // Lanes past the last row re-read it instead of branching around the loads: the lane
     // reduction below then follows straight-line code with the full wave active.
     const long long r = row < rows ? row : rows - 1;
+    // L is loaded with dO and O (every lane of the row reads it), so the three loads share
+    // one memory round trip instead of L waiting for the reduction.
+    const float lr = L[r];
     const u32x4 a = *reinterpret_cast<const u32x4*>(dO + r * D + ch * 8);
     const u32x4 b = *reinterpret_cast<const u32x4*>(O + r * D + ch * 8);
+    asm volatile("" ::"v"(lr));  // keeps the L load here rather than after the reduction
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = dot2_bf16(a[i], b[i], acc);
     acc = group_sum<CH>(acc);
     if (row < rows && ch == 0) {
-      L2[row] = L[row] * kLog2e;
+      L2[row] = lr * kLog2e;
       ND[row] = -acc;
     }
   }
