@@ -32,8 +32,10 @@
  *
  * Errors: argument problems are reported synchronously, before anything is enqueued:
  *   FA_ERROR_INVALID_VALUE  negative size, Nk == 0 while B*H*Nq > 0, a NULL or misaligned
- *                           pointer that the call would touch, non-finite scale, or a
- *                           workspace smaller than fa_backward_workspace_bytes();
+ *                           pointer that the call would touch, non-finite scale, a bf16
+ *                           backward workspace below B * H * Nq * 8 bytes,
+ *                           or a forward workspace that is NULL or not 16-byte aligned
+ *                           while workspace_bytes > 0;
  *   FA_ERROR_NOT_SUPPORTED  unknown dtype, d not in {16, 32, 64, 128}, or a size above the
  *                           limits below;
  *   FA_ERROR_LAUNCH_FAILED  the HIP runtime rejected a kernel launch.
@@ -73,6 +75,19 @@ typedef enum fa_dtype {
 } fa_dtype;
 
 /*
+ * fa_forward_workspace_bytes -- bytes of device workspace fa_forward can use for these
+ * arguments (0 when it needs none, and for arguments fa_forward would reject).
+ *
+ * Small causal bf16 grids (Nq = Nk a multiple of 128, d = 32 or 64, few tiles per head)
+ * spread each pair of query tiles over several workgroups so that every CU has work; their
+ * partial softmax states go to the workspace and a second launch merges them (the same
+ * rescale the online softmax applies between key tiles, problem flash_forward). The size is
+ * (Nq/128) * B * H * ways * 2 * (16*ceil(d/32) + 2) * 128 * 4 bytes, with ways in {2, 4, 8}.
+ */
+FA_API size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                         int64_t Nk, int64_t d, int is_causal);
+
+/*
  * fa_forward -- O = softmax(Q K^T * scale [+ causal mask]) V and L = row logsumexp.
  *
  * Follows problem flash_forward: the kernel walks key tiles with an online softmax
@@ -90,18 +105,30 @@ typedef enum fa_dtype {
  *   scale        multiplies Q K^T (finite; usually 1/sqrt(d))
  *   O            [B,H,Nq,d] dtype, written
  *   L            [B,H,Nq] float32, written (natural-log logsumexp of the scaled scores)
+ *   workspace    device scratch, caller-owned, 16-byte aligned; may be NULL with
+ *                workspace_bytes = 0. With fewer than fa_forward_workspace_bytes bytes the
+ *                call still succeeds: small causal grids then run one workgroup per pair of
+ *                query tiles (slower, same results up to the order of the final merge).
+ *                The call overwrites it; concurrent calls must not share one.
  *   stream       hipStream_t or NULL
  */
 FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                      const void* Q, const void* K, const void* V, int is_causal, float scale,
-                     void* O, float* L, void* stream);
+                     void* O, float* L, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs for these
- * sizes: for bf16, two floats per query row (B * H * Nq * 8 bytes), which hold the
- * preprocessing step's per-row terms L log2(e) and -D; for fp32, 0. Returns 0 for sizes
- * fa_backward would reject. The caller owns the workspace; its contents need no
- * initialisation and are meaningless after the call.
+ * fa_backward_workspace_bytes -- bytes of device workspace fa_backward can use for these
+ * sizes (for fp32, and for sizes fa_backward would reject, 0). For bf16 it is
+ *   - two floats per query row (B * H * Nq * 8 bytes, the minimum fa_backward accepts): the
+ *     preprocessing step's per-row terms L log2(e) and -D, at the start of the workspace;
+ *   - plus, for small square grids (Nq = Nk a multiple of 128, d = 32 or 64, at most 512
+ *     64-row tiles), room for fp32 partial sums: a causal call then spreads each
+ *     workgroup's steps over several workgroups and a second launch adds the partial dQ, dK
+ *     and dV up ((Nq/64) * B * H * ways * 48 * ceil(d/32) * 128 * 4 bytes, ways in {2, 4, 8}).
+ *     With only the minimum, those calls run one workgroup per tile pair (slower; results
+ *     differ only in the order of the final additions).
+ * The caller owns the workspace; its contents need no initialisation and are meaningless
+ * after the call.
  */
 FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
                                    int64_t Nk, int64_t d);
@@ -121,10 +148,11 @@ FA_API size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, 
  *   dO                          [B,H,Nq,d] dtype, upstream gradient
  *   dQ                          [B,H,Nq,d] dtype, written
  *   dK, dV                      [B,H,Nk,d] dtype, written
- *   workspace, workspace_bytes  device scratch of at least fa_backward_workspace_bytes()
- *                               bytes, 4-byte aligned (may be NULL when that is 0); it must
- *                               not overlap any other argument, and calls that share one
- *                               workspace must not run concurrently
+ *   workspace, workspace_bytes  device scratch, 4-byte aligned: at least B * H * Nq * 8
+ *                               bytes for bf16 (may be NULL for fp32), and
+ *                               fa_backward_workspace_bytes() bytes for the fastest path; it
+ *                               must not overlap any other argument, and calls that share
+ *                               one workspace must not run concurrently
  *   stream                      hipStream_t or NULL
  */
 FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["fa_backward", "fa_backward_main", "fa_backward_preprocess",
                                   "fa_backward_workspace_bytes", "fa_forward",
-                                  "fa_status_string"]
+                                  "fa_forward_workspace_bytes", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -60,11 +60,34 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     # bf16: L log2(e) and -D per query row; fp32: none; rejected sizes report 0.
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 64) == 8 * 4096 * 8
+    # Small square grids add room for fp32 partial sums: 64-row tiles x ways x 48 * d/32
+    # floats x 128 lanes (B*H = 1, N = 8192, d = 64: 128 tiles, 4 ways).
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 64) == (
+        8192 * 8 + 128 * 4 * 96 * 128 * 4)
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 2048, 2048, 32) == (
+        2048 * 8 + 32 * 4 * 48 * 128 * 4)
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 128) == 8192 * 8
     assert lib.fa_backward_workspace_bytes(1, 4, 25, 2048, 1024, 128) == 100 * 2048 * 8
     assert lib.fa_backward_workspace_bytes(1, 2, 3, 0, 64, 64) == 0
     assert lib.fa_backward_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 0
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 48) == 0
     assert lib.fa_backward_workspace_bytes(1, -1, 1, 4096, 4096, 64) == 0
+
+
+def test_forward_workspace_sizes(lib):
+    # Small causal bf16 grids (d = 32, 64) use one; everything else needs none.
+    ws = lib.fa_forward_workspace_bytes
+    # B*H = 1, N = 8192, d = 64: 64 tile pairs x 4 ways x 2 records x 34 x 128 floats
+    assert ws(1, 1, 1, 8192, 8192, 64, 1) == 64 * 4 * 2 * 34 * 128 * 4
+    # d = 32: 18 floats per lane in a record
+    assert ws(1, 1, 1, 8192, 8192, 32, 1) == 64 * 4 * 2 * 18 * 128 * 4
+    assert ws(1, 8, 1, 4096, 4096, 64, 1) == 0      # 256 tile pairs fill the CUs already
+    assert ws(1, 1, 1, 8192, 8192, 64, 0) == 0      # not causal
+    assert ws(1, 1, 1, 8192, 8192, 128, 1) == 0     # d = 128 is not split
+    assert ws(1, 1, 1, 8192, 4096, 64, 1) == 0      # Nq != Nk
+    assert ws(0, 1, 1, 8192, 8192, 64, 1) == 0      # fp32
+    assert ws(1, 1, 1, 256, 256, 64, 1) == 0        # runs would be too short
+    assert ws(1, -1, 1, 8192, 8192, 64, 1) == 0     # rejected arguments
 
 
 # A fake, 16-byte aligned address. Only passed where validation must fail first (or where
@@ -74,8 +97,9 @@ BAD = 0x10002  # misaligned
 
 
 def fwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, causal=1, scale=0.125,
-        o=P, lse=P):
-    return lib.fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o, lse, None)
+        o=P, lse=P, ws=None, ws_bytes=0):
+    return lib.fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o, lse, ws, ws_bytes,
+                          None)
 
 
 def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
@@ -93,6 +117,7 @@ def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P,
     (dict(scale=math.inf), 1), (dict(scale=math.nan), 1),
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
     (dict(lse=None), 1), (dict(q=BAD), 1), (dict(o=BAD), 1),
+    (dict(ws=None, ws_bytes=64), 1), (dict(ws=P + 8, ws_bytes=64), 1),
 ])
 def test_forward_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code

@@ -243,6 +243,64 @@ def test_paired_causal_kernels_match_oracle(gpu, case):
     compare(got, full_oracle(inp, True, scale), "bf16")
 
 
+# Causal square shapes few enough in tiles that the forward spreads each tile pair over
+# several workgroups and merges their partial softmax states in a second launch, and the
+# backward spreads each workgroup's steps likewise and adds the partial dQ, dK, dV up
+# (2 or 4 ways here; fa_forward_workspace_bytes > 0, fa_backward_workspace_bytes above the
+# per-row terms).
+SPLIT_WG = [
+    (1, 1, 2048, 64),
+    (2, 3, 2048, 32),
+    (1, 1, 4096, 32),
+    (1, 2, 4096, 64),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_WG, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_forward_split_over_workgroups_matches_oracle(gpu, case):
+    from tiled_attention_causal_amd import forward_workspace_bytes
+    B, H, N, d = case
+    note(f"split-workgroup case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=8700 + N + d + H)
+    assert forward_workspace_bytes(inp["q"], inp["k"], True) > 0
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    heads = [(0, 0), (B - 1, H - 1)]
+    compare(got, full_oracle(inp, True, scale, heads), "bf16", heads)
+
+
+def test_backward_minimum_workspace_matches_split(gpu):
+    """A workspace of only the per-row terms: the same grid runs unsplit, which changes only
+    the order of the partial-sum additions."""
+    from tiled_attention_causal_amd import backward_workspace_bytes, fa_backward, fa_forward
+    inp = make_inputs(1, 2, 4096, 4096, 64, "bf16", index=8900)
+    q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
+    assert backward_workspace_bytes(q, k) > 2 * 4096 * 8
+    o, lse = fa_forward(q, k, v, True, 0.125)
+    g1 = fa_backward(q, k, v, o, lse, do, True, 0.125)
+    g2 = fa_backward(q, k, v, o, lse, do, True, 0.125,
+                     workspace=torch.empty(2 * 4096 * 8, dtype=torch.uint8, device=gpu))
+    torch.cuda.synchronize(gpu)
+    for a, b in zip(g1, g2):
+        a, b = a.float(), b.float()
+        assert torch.all((a - b).abs() <= 2 ** -7 * b.abs() + 1e-3 * b.abs().max())
+
+
+def test_forward_without_workspace_matches_split(gpu):
+    """Less workspace than fa_forward_workspace_bytes: the same grid runs unsplit, which only
+    changes the order of the final merge, so O and L agree to fp32 rounding."""
+    from tiled_attention_causal_amd import fa_forward
+    inp = make_inputs(1, 1, 4096, 4096, 64, "bf16", index=8800)
+    q, k, v = (inp[n].to(gpu) for n in ("q", "k", "v"))
+    o1, l1 = fa_forward(q, k, v, True, 0.125)
+    o2, l2 = fa_forward(q, k, v, True, 0.125,
+                        workspace=torch.empty(0, dtype=torch.uint8, device=gpu))
+    torch.cuda.synchronize(gpu)
+    assert torch.allclose(l1, l2, atol=1e-5, rtol=0)
+    a, b = o1.float(), o2.float()
+    assert torch.all((a - b).abs() <= 2 ** -7 * a.abs().clamp(min=1.0))
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0])
 def test_paired_causal_kernels_unusual_scale(gpu, scale):
     inp = make_inputs(1, 2, 384, 384, 64, "bf16", index=8500)

@@ -4,8 +4,9 @@
 """
 from ._lib import FAError, LIB_PATH, load  # noqa: F401
 from .ops import (FlashAttention, backward_workspace_bytes, default_scale,  # noqa: F401
-                  fa_backward, fa_backward_main, fa_backward_preprocess, fa_forward)
+                  fa_backward, fa_backward_main, fa_backward_preprocess, fa_forward,
+                  forward_workspace_bytes)
 
 __all__ = ["fa_forward", "fa_backward", "fa_backward_preprocess", "fa_backward_main",
-           "backward_workspace_bytes", "FlashAttention", "default_scale", "FAError", "load",
-           "LIB_PATH"]
+           "forward_workspace_bytes", "backward_workspace_bytes", "FlashAttention",
+           "default_scale", "FAError", "load", "LIB_PATH"]

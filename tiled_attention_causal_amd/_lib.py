@@ -23,8 +23,11 @@ FA_DTYPE_BF16 = 1
 _i64 = ctypes.c_int64
 _ptr = ctypes.c_void_p
 SIGNATURES = {
+    "fa_forward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                     ctypes.c_int]),
     "fa_forward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
-                                  ctypes.c_int, ctypes.c_float, _ptr, _ptr, _ptr]),
+                                  ctypes.c_int, ctypes.c_float, _ptr, _ptr, _ptr,
+                                  ctypes.c_size_t, _ptr]),
     "fa_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64]),
     "fa_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                    _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float, _ptr, _ptr,

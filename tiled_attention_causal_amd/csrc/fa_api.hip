@@ -61,20 +61,37 @@ const char* fa_status_string(fa_status status) {
   return "FA_UNKNOWN_STATUS";
 }
 
+// The part of the backward workspace every bf16 call needs: L log2(e) and -D per query row
+// (two floats); the fp32 path needs nothing.
+static size_t backward_rows_bytes(fa_dtype dtype, const fa::Shape& s) {
+  return dtype == FA_DTYPE_BF16 ? (size_t)s.BH * (size_t)s.Nq * 2 * sizeof(float) : 0;
+}
+
 size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                                    int64_t d) {
   fa::Shape s;
   if (check_common(dtype, B, H, Nq, Nk, d, 1.f, 0, &s) != FA_SUCCESS) return 0;
-  // bf16: L log2(e) and -D per query row (two floats); the fp32 path needs nothing.
-  return dtype == FA_DTYPE_BF16 ? (size_t)s.BH * (size_t)s.Nq * 2 * sizeof(float) : 0;
+  const size_t rows = backward_rows_bytes(dtype, s);
+  // Room for the partial sums of small causal grids (used only when the call is causal).
+  return rows > 0 ? rows + fa::bwd_split_workspace_bytes_bf16(s) : 0;
+}
+
+size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                  int64_t d, int is_causal) {
+  fa::Shape s;
+  if (check_common(dtype, B, H, Nq, Nk, d, 1.f, is_causal, &s) != FA_SUCCESS) return 0;
+  return dtype == FA_DTYPE_BF16 ? fa::fwd_workspace_bytes_bf16(s) : 0;
 }
 
 fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                      const void* Q, const void* K, const void* V, int is_causal, float scale,
-                     void* O, float* L, void* stream) {
+                     void* O, float* L, void* workspace, size_t workspace_bytes, void* stream) {
   fa::Shape s;
   const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
   if (st != FA_SUCCESS) return st;
+  if (workspace_bytes > 0 &&
+      (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0))
+    return FA_ERROR_INVALID_VALUE;
   if ((int64_t)s.BH * Nq == 0) return FA_SUCCESS;
   if (Nk == 0) return FA_ERROR_INVALID_VALUE;  // softmax over no keys
   if (bad_ptr(Q) || bad_ptr(K) || bad_ptr(V) || bad_ptr(O) || L == nullptr ||
@@ -83,7 +100,8 @@ fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
-    e = fa::launch_fwd_bf16(s, Q, K, V, O, L, hs);
+    e = fa::launch_fwd_bf16(s, Q, K, V, O, L, static_cast<float*>(workspace), workspace_bytes,
+                            hs);
   else
     e = fa::launch_fwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
                            static_cast<const float*>(V), static_cast<float*>(O), L, hs);
@@ -98,7 +116,7 @@ static fa_status check_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq
                                 size_t workspace_bytes, fa::Shape* s, bool* nothing) {
   const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, s);
   if (st != FA_SUCCESS) return st;
-  const size_t ws_need = fa_backward_workspace_bytes(dtype, B, H, Nq, Nk, d);
+  const size_t ws_need = backward_rows_bytes(dtype, *s);
   if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
   if (ws_need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
     return FA_ERROR_INVALID_VALUE;
@@ -121,7 +139,7 @@ fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t N
   // Keys play no part here; Nk = 0 keeps the size checks to the query side.
   const fa_status st = check_common(dtype, B, H, Nq, 0, d, 1.f, 0, &s);
   if (st != FA_SUCCESS) return st;
-  const size_t ws_need = fa_backward_workspace_bytes(dtype, B, H, Nq, 0, d);
+  const size_t ws_need = backward_rows_bytes(dtype, s);
   if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
   if (ws_need == 0) return FA_SUCCESS;  // fp32, or no query rows: nothing to precompute
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 ||
@@ -147,7 +165,7 @@ fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
     e = fa::launch_bwd_main_bf16(s, Q, K, V, dO, dQ, dK, dV,
-                                 static_cast<const float*>(workspace), hs);
+                                 static_cast<const float*>(workspace), workspace_bytes, hs);
   else
     e = fa::launch_bwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
                            static_cast<const float*>(V), static_cast<const float*>(O), L,

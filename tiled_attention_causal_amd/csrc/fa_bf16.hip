@@ -485,7 +485,8 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 template <int D>
 __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg) {
+    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg, int ns,
+    float* __restrict__ part) {
   constexpr int NP = 4, BK = 64;
   constexpr int DS = D / 16, DB = (D + 31) / 32;
   using KTile = Tile<BK, D>;
@@ -497,7 +498,8 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
 
   const int T = N / 64, half = T / 2;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / half, i = lid % half;
+  const int sw = lid % ns, pid = lid / ns;  // this workgroup's share of tile pair pid
+  const int bh = pid / half, i = pid % half;
   const int tA = T - 1 - i, tB = i, nA = T - i, S = T + 1;
   const rsrc_t Qr = make_rsrc(Q + (size_t)bh * N * D, (uint32_t)N * D * 2);
   const rsrc_t Kr = make_rsrc(K + (size_t)bh * N * D, (uint32_t)N * D * 2);
@@ -505,7 +507,8 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int pr = w >> 1, wp = w & 1;
-  const int st = pr * S / NP, en = (pr + 1) * S / NP;  // this pair's run of the sequence
+  const int NR = NP * ns;  // runs per tile pair, over all ns workgroups
+  const int st = (sw * NP + pr) * S / NR, en = (sw * NP + pr + 1) * S / NR;  // this pair's run
   const float cs = fabsf(scale);
   const float c = exp2_coef(scale);
 
@@ -605,13 +608,13 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   // Partials of the tile being merged: slot p holds tile A iff p's run ends within A; the
   // crossing record holds A's part from the run that crosses into B, if one does.
   auto included = [&](int p) {
-    const int sp = p * S / NP, ep = (p + 1) * S / NP;
+    const int sp = (sw * NP + p) * S / NR, ep = (sw * NP + p + 1) * S / NR;
     return sp < ep && (ep <= nA) == mergeA;
   };
   bool cross = false;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sp = p * S / NP, ep = (p + 1) * S / NP;
+    const int sp = (sw * NP + p) * S / NR, ep = (sw * NP + p + 1) * S / NR;
     cross |= sp < nA && nA < ep;
   }
   cross = cross && mergeA;
@@ -636,10 +639,82 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   for (int p = 0; p < NP; ++p)
     if (included(p)) add(slots + p * XS * 128);
   if (cross) add(park_cross);
+  if (ns > 1) {
+    // This workgroup's partial (m, l, unnormalised O) for the tile, in the component-major
+    // record layout; fwd_split_combine_kernel merges the ns records. A workgroup with no
+    // part of the tile writes m = -inf, l = 0.
+    float* x = part + ((size_t)pid * ns + sw) * 2 * (XS * 128) + (mergeA ? 0 : XS * 128) +
+               wp * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[db][r];
+    x[16 * DB * 128] = mm;
+    x[(16 * DB + 1) * 128] = lsum;
+    return;
+  }
   const float lt = halves_sum(lsum);
   const int row = 64 * (mergeA ? tA : tB) + 32 * wp + l32;
   store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
   if (g == 0) Lout[(size_t)bh * N + row] = mm * cs + logf(lt);
+}
+
+
+// Merges the ns partial records fwd_causal_split_kernel wrote for each 64-row tile (when it
+// spreads a tile pair over ns <= kMaxWays workgroups) with the online-softmax rescale, and
+// stores O and L. One workgroup per tile with 128 threads per 32-column block: thread t takes
+// record lane t % 128 (lane = row, as in the split kernel) and column block t / 128, so every
+// load is coalesced and all of a thread's loads are independent. A record from a workgroup
+// with no part of the tile has m = -inf and l = O = 0, and so gets weight exp2(-inf) = 0.
+template <int D>
+__global__ __launch_bounds__(128 * ((D + 31) / 32)) void fwd_split_combine_kernel(
+    const float* __restrict__ part, bf16* __restrict__ O, float* __restrict__ Lout, int N,
+    float scale, int ns) {
+  constexpr int DB = (D + 31) / 32, XS = 16 * DB + 2, MAXW = 8;
+  const int T = N / 64, half = T / 2;
+  const int tile = blockIdx.x % T, bh = blockIdx.x / T;
+  const bool isA = tile >= half;  // tile pair i holds A = T-1-i and B = i
+  const int i = isA ? T - 1 - tile : tile;
+  const int slot = threadIdx.x & 127, db = threadIdx.x >> 7;
+  const int lane = slot & 63, wp = slot >> 6, g = lane >> 5, l32 = lane & 31;
+  const float c = exp2_coef(scale), cs = fabsf(scale);
+  const float* x0 = part + (size_t)(bh * half + i) * ns * 2 * (XS * 128) +
+                    (isA ? 0 : XS * 128) + slot;
+  const size_t stride = 2 * (XS * 128);
+  float mw[MAXW], lw[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    mw[w] = w < ns ? x0[w * stride + 16 * DB * 128] : -INFINITY;
+    lw[w] = w < ns ? x0[w * stride + (16 * DB + 1) * 128] : 0.f;
+  }
+  float mm = mw[0];
+#pragma unroll
+  for (int w = 1; w < MAXW; ++w) mm = fmaxf(mm, mw[w]);
+  f32x16 o = zero16();
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    if (w < ns) {
+      const float f = fast_exp2((mw[w] - mm) * c);
+      const float* x = x0 + w * stride + 16 * db * 128;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] += f * x[r * 128];
+      lsum += f * lw[w];
+    }
+  }
+  const float lt = halves_sum(lsum);
+  const float inv = 1.f / lt;
+  const int row = 64 * tile + 32 * wp + l32;
+  bf16* orow = O + ((size_t)bh * N + row) * D;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d0 = 32 * db + 8 * j + 4 * g;
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[4 * j + e] * inv);
+    *reinterpret_cast<bf16x4*>(orow + d0) = v;
+  }
+  if (db == 0 && g == 0) Lout[(size_t)bh * N + row] = mm * cs + logf(lt);
 }
 
 // ----------------------------------------------------------------------------- backward
@@ -1026,7 +1101,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
   }
 }
 
-// Runs step(n, cur) for n = 0 .. nsteps-1 over tiles that fetch(n, dst) loads straight into
+// Runs step(n, cur) for n = first .. last-1 over tiles that fetch(n, dst) loads straight into
 // LDS, two tiles ahead, through three buffers. Each step issues the loads of tile n+2, runs,
 // then waits for tile n+1 only (vmcnt(KEEP), KEEP = vector-memory instructions one fetch
 // issues per wave) and meets the other waves at an LDS-only barrier. The loop sits in one
@@ -1036,14 +1111,15 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
 // wait for them. A step that issues other vector-memory instructions must wait for all of
 // them itself before returning.
 template <int KEEP, class Fetch, class Step>
-__device__ __forceinline__ void stream3(int nsteps, bf16* __restrict__ b0, bf16* __restrict__ b1,
-                                        bf16* __restrict__ b2, Fetch&& fetch, Step&& step) {
-  if (nsteps > 0) fetch(0, b0);
-  if (nsteps > 1) fetch(1, b1);
+__device__ __forceinline__ void stream3(int first, int last, bf16* __restrict__ b0,
+                                        bf16* __restrict__ b1, bf16* __restrict__ b2,
+                                        Fetch&& fetch, Step&& step) {
+  if (first < last) fetch(first, b0);
+  if (first + 1 < last) fetch(first + 1, b1);
   wait_vmem();
   __syncthreads();
   auto one = [&](int n, bf16* cur, bf16* pre) {
-    const bool more = n + 2 < nsteps;
+    const bool more = n + 2 < last;
     if (more) fetch(n + 2, pre);
     step(n, cur);
     if (more)
@@ -1052,11 +1128,36 @@ __device__ __forceinline__ void stream3(int nsteps, bf16* __restrict__ b0, bf16*
       wait_vmem();
     lds_barrier();
   };
-  for (int n = 0; n < nsteps; n += 3) {
+  for (int n = first; n < last; n += 3) {
     one(n, b0, b2);
-    if (n + 1 < nsteps) one(n + 1, b1, b0);
-    if (n + 2 < nsteps) one(n + 2, b2, b1);
+    if (n + 1 < last) one(n + 1, b1, b0);
+    if (n + 2 < last) one(n + 2, b2, b1);
   }
+}
+
+// Partial sums of the split backward: an accumulator set stored unscaled as fp32 rows, the
+// layout store_rows_from_acc gives bf16 outputs (lane owns row `out_row`; register r of block
+// db holds column 32db + 8(r/4) + 4g + r%4), or zeros for a share with no step of the tile.
+template <int D>
+__device__ __forceinline__ void put_rows_f32(float* out_row, const f32x16 (&acc)[(D + 31) / 32],
+                                             int g) {
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[db][4 * j + i];
+      *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = v;
+    }
+}
+template <int D>
+__device__ __forceinline__ void put_zero_rows_f32(float* out_row, int g) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = z;
 }
 
 // Causal backward with complementary tile pairing, for Nq = Nk = N, N % 128 == 0 (the
@@ -1075,7 +1176,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ L2, const float* __restrict__ ND, const bf16* __restrict__ dO,
     bf16* __restrict__ dQ, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale,
-    int neg) {
+    int neg, int ns, float* __restrict__ kvpart, float* __restrict__ qpart) {
   using B = Bwd<D>;
   constexpr int DS = B::DS, DB = B::DB;
   constexpr int SM = B::KV_BUF > B::Q_BUF ? B::KV_BUF : B::Q_BUF;
@@ -1084,7 +1185,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
 
   const int T = N / 64, half = T / 2;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / T, idx = lid % T;
+  const int sw = lid % ns, pid = lid / ns;  // this workgroup's share of workgroup pid's steps
+  const int bh = pid / T, idx = pid % T;
   const size_t o = (size_t)bh * N * D;
   const uint32_t nb = (uint32_t)N * D * 2;
   const rsrc_t Qr = make_rsrc(Q + o, nb), dOr = make_rsrc(dO + o, nb);
@@ -1096,7 +1198,18 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
   const int pr = w >> 1, wp = w & 1;  // pair, wave in pair
   const float c = exp2_coef(scale);
   const int nsteps = T + 1;
+  // With ns > 1 this workgroup runs steps [n_lo, n_hi) of both pairs' runs and writes fp32
+  // partial sums per 64-row tile (records of component-major lanes, as the merge below) for
+  // bwd_split_combine_kernel to add up.
+  const int n_lo = sw * nsteps / ns, n_hi = (sw + 1) * nsteps / ns;
   constexpr int XS = 2 * 16 * DB;  // merge record per lane: up to two accumulator sets
+  // Partial sums (ns > 1) are fp32 [64 rows][D] tiles: for key tile t and share sw, dK^T at
+  // kvpart + ((bh T + t) ns + sw) 2 * 64 D and dV^T right after it; dQ^T at qpart + ((bh T +
+  // t) ns + sw) 64 D. part_row gives this lane's row (32 wp + l32) in one of them.
+  auto part_row = [&](float* base, int tile, int tensors, int which) {
+    return base + ((((size_t)bh * T + tile) * ns + sw) * tensors + which) * (64 * D) +
+           (32 * wp + l32) * D;
+  };
 
   if (idx < half) {
     // ---------------------------------------------------------------- dK / dV workgroup
@@ -1107,7 +1220,9 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     auto mt_of = [&](int n) {
       return pr == 0 ? 2 * tA + n : (n < nB ? 2 * tB + n : 2 * tA + nsteps + (n - nB));
     };
-    int kt = kt_of(0);
+    // The first tile, written out rather than as kt_of(n_lo): through the lambda, hipcc 7.2
+    // keeps tA and tB in scratch memory and reloads them every step.
+    int kt = (pr == 1 && n_lo < nB) ? tB + 0 : tA + 0;
     int krow = 64 * kt + 32 * wp + l32;
     bf16x8 kf[DS], vf[DS];
     load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
@@ -1120,7 +1235,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     // Per wave, one fetch issues NKIB/2 loads for each of Q and dO, and one for L2 or ND.
     constexpr int kKeep = B::MTile::NKIB + 1;
     stream3<kKeep>(
-        nsteps, smem[pr][0], smem[pr][1], smem[pr][2],
+        n_lo, n_hi, smem[pr][0], smem[pr][1], smem[pr][2],
         [&](int n, bf16* dst) { kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n), dst, wp, lane); },
         [&](int n, bf16* buf) {
           const int m0 = 32 * mt_of(n);
@@ -1132,8 +1247,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
                              lane, l32, g);
           }
           if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
-            store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
-            store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+            if (ns > 1) {
+              put_rows_f32<D>(part_row(kvpart, tB, 2, 0), dkt, g);
+              put_rows_f32<D>(part_row(kvpart, tB, 2, 1), dvt, g);
+            } else {
+              store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
+              store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
               dvt[db] = zero16();
@@ -1147,7 +1267,19 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end). The
     // merge record is component-major (component k of wave wp's lane at k * 128 + wp * 64 +
     // lane), so the exchange is free of bank conflicts.
-    const bool p1_has_A = nsteps > nB;
+    const bool p1_has_A = n_hi > nB;
+    // B's partial from this share: written at the switch when B completes inside the share
+    // (n_lo < nB <= n_hi); here when the share ends before B completes (pair 1's sums are
+    // B's), or as zeros when the share has no B step.
+    if (ns > 1 && pr == 1) {
+      if (n_lo >= nB) {
+        put_zero_rows_f32<D>(part_row(kvpart, tB, 2, 0), g);
+        put_zero_rows_f32<D>(part_row(kvpart, tB, 2, 1), g);
+      } else if (n_hi < nB) {
+        put_rows_f32<D>(part_row(kvpart, tB, 2, 0), dkt, g);
+        put_rows_f32<D>(part_row(kvpart, tB, 2, 1), dvt, g);
+      }
+    }
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
     static_assert(2 * 64 * XS * sizeof(float) <= sizeof(smem), "merge area must fit");
     if (pr == 1 && p1_has_A) {
@@ -1172,8 +1304,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
             dvt[db][r] += x[(16 * (DB + db) + r) * 128];
           }
       }
-      store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
-      store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+      if (ns > 1) {
+        put_rows_f32<D>(part_row(kvpart, tA, 2, 0), dkt, g);
+        put_rows_f32<D>(part_row(kvpart, tA, 2, 1), dvt, g);
+      } else {
+        store_rows_from_acc<D>(dK + o + (size_t)krow * D, dkt, scale, g);
+        store_rows_from_acc<D>(dV + o + (size_t)krow * D, dvt, 1.f, g);
+      }
     }
   } else {
     // ------------------------------------------------------------------------ dQ workgroup
@@ -1182,7 +1319,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     const int nB = 2 * (i + 1);
     auto qt_of = [&](int n) { return (pr == 0 || n >= nB) ? tA : tB; };
     auto kt_of = [&](int n) { return pr == 0 ? n : (n < nB ? n : nsteps + (n - nB)); };
-    int qt = qt_of(0);
+    int qt = (pr == 1 && n_lo < nB) ? tB + 0 : tA + 0;  // as kt above
     int qrow = 64 * qt + 32 * wp + l32;
     QRow<D> row;
     row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
@@ -1192,7 +1329,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     // Per wave, one fetch issues NKIB/2 loads for each of K and V.
     constexpr int kKeep = B::MTile::NKIB;
     stream3<kKeep>(
-        nsteps, smem[pr][0], smem[pr][1], smem[pr][2],
+        n_lo, n_hi, smem[pr][0], smem[pr][1], smem[pr][2],
         [&](int n, bf16* dst) {
           B::MTile::template load<2>(Kr, 32 * kt_of(n), dst, wp, lane);
           B::MTile::template load<2>(Vr, 32 * kt_of(n), dst + B::T, wp, lane);
@@ -1207,7 +1344,10 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
                             qrow - n0 - 4 * g, lane, l32, g);
           }
           if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
-            store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
+            if (ns > 1)
+              put_rows_f32<D>(part_row(qpart, tB, 1, 0), dqt, g);
+            else
+              store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
 #pragma unroll
             for (int db = 0; db < DB; ++db) dqt[db] = zero16();
             qt = tA;
@@ -1215,7 +1355,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
             row.load(Qr, dOr, L2r, NDr, qrow, g, neg);  // waits for all its loads
           }
         });
-    const bool p1_has_A = nsteps > nB;
+    const bool p1_has_A = n_hi > nB;
+    if (ns > 1 && pr == 1) {  // as for dK/dV above
+      if (n_lo >= nB)
+        put_zero_rows_f32<D>(part_row(qpart, tB, 1, 0), g);
+      else if (n_hi < nB)
+        put_rows_f32<D>(part_row(qpart, tB, 1, 0), dqt, g);
+    }
     float* xf = reinterpret_cast<float*>(&smem[0][0][0]);
     if (pr == 1 && p1_has_A) {
       float* x = xf + wp * 64 + lane;
@@ -1233,26 +1379,122 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
 #pragma unroll
           for (int r = 0; r < 16; ++r) dqt[db][r] += x[(16 * db + r) * 128];
       }
-      store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
+      if (ns > 1)
+        put_rows_f32<D>(part_row(qpart, tA, 1, 0), dqt, g);
+      else
+        store_rows_from_acc<D>(dQ + o + (size_t)qrow * D, dqt, scale, g);
     }
   }
 }
 
+// Adds the ns partial [64][D] fp32 tiles bwd_causal_paired_kernel wrote for each 64-row tile
+// when it spreads every workgroup's steps over ns workgroups, scales dK and dQ, and stores
+// dQ, dK and dV. Each thread sums one float4 of one tensor over the ns shares (independent
+// loads, consecutive threads on consecutive addresses); a tile's three tensors take
+// 3 * 64 * D / 1024 workgroups of 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_split_combine_kernel(
+    const float* __restrict__ kvpart, const float* __restrict__ qpart, bf16* __restrict__ dQ,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale, int ns) {
+  constexpr int MAXW = 8, TILE = 64 * D, BLOCKS = 3 * TILE / 1024;  // per tile
+  const int T = N / 64;
+  const int tb = blockIdx.x / BLOCKS, part = blockIdx.x % BLOCKS;
+  const int tile = tb % T, bh = tb / T;
+  const size_t base = ((size_t)bh * T + tile) * ns;
+  const int e = part * 1024 + 4 * threadIdx.x;
+  const int tensor = e / TILE, k = e % TILE;  // 0: dK, 1: dV, 2: dQ
+  const float* x = tensor < 2 ? kvpart + base * 2 * TILE + tensor * TILE + k
+                              : qpart + base * TILE + k;
+  const size_t stride = tensor < 2 ? 2 * TILE : TILE;
+  f32x4 v[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < ns) v[w] = *reinterpret_cast<const f32x4*>(x + w * stride);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < ns) acc += v[w];
+  const float mul = tensor == 1 ? 1.f : scale;
+  bf16* out = tensor == 0 ? dK : (tensor == 1 ? dV : dQ);
+  bf16x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * mul);
+  *reinterpret_cast<bf16x4*>(out + ((size_t)bh * N + 64 * tile) * D + k) = o;
+}
+
+// Workgroups per workgroup of the causal paired backward (d = 32, 64): small grids spread each
+// workgroup's T+1 steps over up to kMaxWays workgroups, doubling while the grid stays within
+// two workgroups per CU and every share keeps at least kMinShare steps.
+constexpr int kMinShare = 8;
+int bwd_split_ways(const Shape& s) {
+  if (s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32 || s.d > 64) return 1;
+  const long long wgs = (long long)(s.Nq / 64) * s.BH;
+  if (wgs > 2 * kNumCUs) return 1;
+  const int steps = s.Nq / 64 + 1;
+  int ns = 1;
+  while (ns < 8 && wgs * ns * 2 <= 2 * kNumCUs && steps / (ns * 2) >= kMinShare) ns *= 2;
+  return ns;
+}
+
+// Workgroups per tile pair of the causal split forward (d = 32, 64). Small grids spread each
+// pair's key steps over up to kMaxWays workgroups, doubling while the grid still fits the CUs
+// and every wave pair keeps a run of at least kMinRun key steps; larger grids use one.
+constexpr int kMinRun = 4, kMaxWays = 8;
+static_assert(kMaxWays <= 8, "fwd_split_combine_kernel merges at most 8 records per tile");
+int fwd_split_ways(const Shape& s) {
+  if (!s.causal || s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32 || s.d > 64) return 1;
+  const long long pairs = (long long)(s.Nq / 128) * s.BH;
+  if (pairs > kNumCUs) return 1;
+  const int steps = s.Nq / 64 + 1, np = 4;  // key steps per tile pair, wave pairs per workgroup
+  int ns = 1;
+  while (ns < kMaxWays && pairs * ns * 2 <= kNumCUs && steps / (np * ns * 2) >= kMinRun) ns *= 2;
+  return ns;
+}
+
+}  // namespace
+
+size_t fwd_workspace_bytes_bf16(const Shape& s) {
+  const int ns = fwd_split_ways(s);
+  if (ns == 1) return 0;
+  const size_t xs = 16 * ((s.d + 31) / 32) + 2;  // floats per lane in a partial record
+  return (size_t)(s.Nq / 128) * s.BH * ns * 2 * xs * 128 * sizeof(float);
+}
+
+size_t bwd_split_workspace_bytes_bf16(const Shape& s) {
+  const int ns = bwd_split_ways(s);
+  if (ns == 1) return 0;
+  // Per 64-row tile and share: fp32 [64][d] tiles of dK^T, dV^T and dQ^T.
+  return (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
+}
+
+namespace {
+
 template <int D, bool CAUSAL>
 hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, void* O, float* L,
-                 hipStream_t stream) {
+                 float* ws, size_t ws_bytes, hipStream_t stream) {
   // Pairing pays off only when one 128-query tile per workgroup leaves CUs idle or runs a
   // single wave per SIMD anyway; larger grids keep the plain kernel (shared K/V stream, two
   // waves per SIMD).
   if constexpr (CAUSAL && D >= 32) {
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 128) * s.BH <= kNumCUs) {
-      const long long grid = (long long)(s.Nq / 128) * s.BH;
-      if constexpr (D <= 64)
-        hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3((unsigned)grid), dim3(512), 0,
-                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
-      else
-        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
+      const long long pairs = (long long)(s.Nq / 128) * s.BH;
+      if constexpr (D <= 64) {
+        int ns = fwd_split_ways(s);
+        if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
+        hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3((unsigned)(pairs * ns)),
+                           dim3(512), 0, stream, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, (bf16*)O, L, s.Nq, s.scale, s.scale < 0.f ? 1 : 0,
+                           ns, ws);
+        if (ns > 1) {
+          const hipError_t e = hipGetLastError();
+          if (e != hipSuccess) return e;
+          hipLaunchKernelGGL((fwd_split_combine_kernel<D>),
+                             dim3((unsigned)((long long)s.BH * (s.Nq / 64))),
+                             dim3(128 * ((D + 31) / 32)), 0,
+                             stream, (const float*)ws, (bf16*)O, L, s.Nq, s.scale, ns);
+        }
+      } else
+        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
                            stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
                            s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
       return hipGetLastError();
@@ -1281,7 +1523,8 @@ hipError_t bwd_prep_t(const Shape& s, const void* O, const float* L, const void*
 
 template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
-                 void* dQ, void* dK, void* dV, const float* ws, hipStream_t stream) {
+                 void* dQ, void* dK, void* dV, const float* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   const long long rows = (long long)s.BH * s.Nq;
   const float* L2 = ws;
   const float* ND = ws + rows;
@@ -1291,11 +1534,28 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   // instantiation, so it is not built.)
   if constexpr (CAUSAL && D >= 32 && D <= 64) {
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 2 * kNumCUs) {
-      const long long grid = (long long)(s.Nq / 64) * s.BH;
-      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
-                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
+      const long long wgs = (long long)(s.Nq / 64) * s.BH;
+      // Partial sums for split grids follow the two per-row arrays in the workspace.
+      int ns = bwd_split_ways(s);
+      const size_t split_bytes = bwd_split_workspace_bytes_bf16(s);
+      if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes ||
+                     (reinterpret_cast<uintptr_t>(ws) & 15u) != 0))
+        ns = 1;  // the partial tiles are written and read 16 bytes at a time
+      float* kvpart = const_cast<float*>(ws) + 2 * rows;
+      float* qpart = kvpart + (size_t)wgs * ns * 2 * 64 * D;  // after dK^T, dV^T of every tile
+      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(wgs * ns)), dim3(256),
+                         0, stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
                          (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
-                         s.scale < 0.f ? 1 : 0);
+                         s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
+      if (ns > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_split_combine_kernel<D>),
+                           dim3((unsigned)(wgs * (3 * 64 * D / 1024))), dim3(256), 0, stream,
+                           (const float*)kvpart,
+                           (const float*)qpart, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
+                           ns);
+      }
       return hipGetLastError();
     }
   }
@@ -1309,11 +1569,12 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
 }  // namespace
 
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V, void* O,
-                           float* L, hipStream_t stream) {
-#define FA_FWD(DD)                                                              \
-  case DD:                                                                      \
-    return s.causal ? fwd_t<DD, true>(s, Q, K, V, O, L, stream)                 \
-                    : fwd_t<DD, false>(s, Q, K, V, O, L, stream);
+                           float* L, float* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+#define FA_FWD(DD)                                                                             \
+  case DD:                                                                                     \
+    return s.causal ? fwd_t<DD, true>(s, Q, K, V, O, L, workspace, workspace_bytes, stream)    \
+                    : fwd_t<DD, false>(s, Q, K, V, O, L, workspace, workspace_bytes, stream);
   switch (s.d) {
     FA_FWD(16)
     FA_FWD(32)
@@ -1343,11 +1604,13 @@ hipError_t launch_bwd_prep_bf16(const Shape& s, const void* O, const float* L, c
 
 hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                                 const void* dO, void* dQ, void* dK, void* dV,
-                                const float* workspace, hipStream_t stream) {
-#define FA_BWD(DD)                                                                          \
-  case DD:                                                                                  \
-    return s.causal ? bwd_t<DD, true>(s, Q, K, V, dO, dQ, dK, dV, workspace, stream)        \
-                    : bwd_t<DD, false>(s, Q, K, V, dO, dQ, dK, dV, workspace, stream);
+                                const float* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+#define FA_BWD(DD)                                                                              \
+  case DD:                                                                                      \
+    return s.causal                                                                             \
+               ? bwd_t<DD, true>(s, Q, K, V, dO, dQ, dK, dV, workspace, workspace_bytes, stream) \
+               : bwd_t<DD, false>(s, Q, K, V, dO, dQ, dK, dV, workspace, workspace_bytes, stream);
   switch (s.d) {
     FA_BWD(16)
     FA_BWD(32)

@@ -15,15 +15,25 @@ struct Shape {
   float scale;
 };
 
+// Small causal grids spread each tile pair over several workgroups, whose partial results
+// go to `workspace` (fwd_workspace_bytes_bf16 bytes) and are merged by a second launch. With a
+// smaller workspace (or none) those grids run one workgroup per tile pair.
+size_t fwd_workspace_bytes_bf16(const Shape& s);
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V, void* O,
-                           float* L, hipStream_t stream);
+                           float* L, float* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 // The bf16 backward is two launches sharing `workspace` (2 * BH * Nq floats): the first writes
 // per-row terms (L log2(e) and -D) from O, L and dO, the second reads them.
 hipError_t launch_bwd_prep_bf16(const Shape& s, const void* O, const float* L, const void* dO,
                                 float* workspace, hipStream_t stream);
+// Small causal grids (Nq = Nk, d = 32 or 64) spread each workgroup's steps over several
+// workgroups when the workspace also holds bwd_split_workspace_bytes_bf16 bytes of fp32 partial
+// sums after the per-row terms; a second launch adds them up.
+size_t bwd_split_workspace_bytes_bf16(const Shape& s);
 hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                                 const void* dO, void* dQ, void* dK, void* dV,
-                                const float* workspace, hipStream_t stream);
+                                const float* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           float* O, float* L, hipStream_t stream);
 hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const float* V,

@@ -43,10 +43,20 @@ def _raise(status: int, where: str):
         raise _lib.FAError(status, where)
 
 
+def forward_workspace_bytes(q: torch.Tensor, k: torch.Tensor, is_causal: bool) -> int:
+    """Bytes of device workspace fa_forward can use for these shapes (0: none)."""
+    B, H, Nq, d = q.shape
+    return _lib.load().fa_forward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, k.shape[2], d,
+                                                  int(bool(is_causal)))
+
+
 def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
                scale: float | None = None, out: torch.Tensor | None = None,
-               lse: torch.Tensor | None = None):
-    """O, L = attention forward on [B, H, N, d] tensors (bf16 or fp32)."""
+               lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """O, L = attention forward on [B, H, N, d] tensors (bf16 or fp32).
+
+    `workspace` (uint8, on q's device) is allocated when not given and the shapes can use
+    one (forward_workspace_bytes); pass a tensor to reuse it across calls."""
     lib = _lib.load()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, Nq, d]")
@@ -64,9 +74,19 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: boo
     _check("out", out, (B, H, Nq, d), q.dtype, q.device)
     _check("lse", lse, (B, H, Nq), torch.float32, q.device)
     sc = default_scale(d) if scale is None else float(scale)
+    if workspace is None:
+        need = lib.fa_forward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, Nk, d,
+                                              int(bool(is_causal)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = lib.fa_forward(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
                         v.data_ptr(), int(bool(is_causal)), sc, out.data_ptr(), lse.data_ptr(),
-                        _stream_ptr(q))
+                        ws_ptr or None, ws_bytes, _stream_ptr(q))
     _raise(st, "fa_forward")
     return out, lse
 
@@ -89,8 +109,12 @@ def _backward_args(q, k, v, o, lse, do, dq, dk, dv, workspace):
         _check(name, t, (B, H, n, d), dt, q.device)
     ws_bytes = lib.fa_backward_workspace_bytes(_DTYPES[dt], B, H, Nq, Nk, d)
     if workspace is not None:
-        if workspace.device != q.device or workspace.nbytes < ws_bytes:
-            raise ValueError(f"workspace must be a {ws_bytes}-byte tensor on {q.device}")
+        # bf16 needs two floats per query row; fa_backward_workspace_bytes may ask for more
+        # (partial sums that let small causal grids use every CU), which is optional.
+        need = B * H * Nq * 8 if dt == torch.bfloat16 else 0
+        if workspace.device != q.device or workspace.nbytes < need:
+            raise ValueError(f"workspace must be a tensor of at least {need} bytes "
+                             f"({ws_bytes} for the fastest path) on {q.device}")
         ws, ws_bytes = workspace, workspace.nbytes
     else:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
