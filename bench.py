@@ -117,7 +117,7 @@ def time_workload(w, steps, warmup):
     from seeded_inputs import workload_inputs
     from tiled_attention_causal_amd import (backward_workspace_bytes, fa_backward,
                                             fa_backward_main, fa_backward_preprocess,
-                                            fa_forward)
+                                            fa_forward, forward_workspace_bytes)
 
     dev = torch.device("cuda:0")
     inp = workload_inputs(w)
@@ -126,10 +126,11 @@ def time_workload(w, steps, warmup):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(1, backward_workspace_bytes(q, k)), dtype=torch.uint8, device=dev)
+    fws = torch.empty(forward_workspace_bytes(q, k, w.causal), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(warmup):
@@ -150,7 +151,7 @@ def time_workload(w, steps, warmup):
     torch.cuda.synchronize(dev)
     for i in range(steps):
         ev[i][0].record(stream)
-        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse, workspace=fws)
         ev[i][1].record(stream)
         fa_backward_preprocess(o, lse, do, ws)
         ev[i][2].record(stream)

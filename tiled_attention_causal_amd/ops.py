@@ -7,6 +7,7 @@ saved for the backward is the logsumexp L.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import torch
@@ -43,11 +44,15 @@ def _raise(status: int, where: str):
         raise _lib.FAError(status, where)
 
 
+@functools.lru_cache(maxsize=256)
+def _forward_ws_bytes(dtype: int, B: int, H: int, Nq: int, Nk: int, d: int, causal: int) -> int:
+    return _lib.load().fa_forward_workspace_bytes(dtype, B, H, Nq, Nk, d, causal)
+
+
 def forward_workspace_bytes(q: torch.Tensor, k: torch.Tensor, is_causal: bool) -> int:
     """Bytes of device workspace fa_forward can use for these shapes (0: none)."""
     B, H, Nq, d = q.shape
-    return _lib.load().fa_forward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, k.shape[2], d,
-                                                  int(bool(is_causal)))
+    return _forward_ws_bytes(_DTYPES[q.dtype], B, H, Nq, k.shape[2], d, int(bool(is_causal)))
 
 
 def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
@@ -75,8 +80,7 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: boo
     _check("lse", lse, (B, H, Nq), torch.float32, q.device)
     sc = default_scale(d) if scale is None else float(scale)
     if workspace is None:
-        need = lib.fa_forward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, Nk, d,
-                                              int(bool(is_causal)))
+        need = _forward_ws_bytes(_DTYPES[q.dtype], B, H, Nq, Nk, d, int(bool(is_causal)))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr, ws_bytes = 0, 0
