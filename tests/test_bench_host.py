@@ -38,6 +38,10 @@ def test_kernel_names_follow_dispatch():
         "fwd_kernel<64, false>", "bwd_kernel<64, false>")
     assert bench.kernel_names(WORKLOADS["long_n16384_d128"]) == (
         "fwd_kernel<128, true>", "bwd_kernel<128, true>")
+    assert bench.kernel_names(WORKLOADS["gpt_small"]) == (
+        "fwd_causal_paired_kernel<64>", "bwd_causal_paired_kernel<64>")
+    assert bench.kernel_names(WORKLOADS["xl_causal"]) == (
+        "fwd_kernel<64, true>", "bwd_kernel<64, true>")
 
 
 def test_more_than_one_gpu_is_refused():

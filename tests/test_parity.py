@@ -269,6 +269,23 @@ def test_forward_split_over_workgroups_matches_oracle(gpu, case):
     compare(got, full_oracle(inp, True, scale, heads), "bf16", heads)
 
 
+# Grids between one and two tile pairs per CU: the forward takes the four-wave paired kernel
+# (two per CU), the backward the paired kernel (up to three per CU).
+MID = [(4, 9, 1024, 32), (2, 17, 1024, 64)]
+
+
+@pytest.mark.parametrize("case", MID, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_mid_grids_take_paired_kernels(gpu, case):
+    B, H, N, d = case
+    assert 256 < (N // 128) * B * H <= 512
+    note(f"mid-grid case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=9000 + H + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    heads = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    compare(got, full_oracle(inp, True, scale, heads), "bf16", heads)
+
+
 def test_backward_minimum_workspace_matches_split(gpu):
     """A workspace of only the per-row terms: the same grid runs unsplit, which changes only
     the order of the partial-sum additions."""

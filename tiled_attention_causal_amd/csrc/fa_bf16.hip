@@ -1474,10 +1474,19 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
                  float* ws, size_t ws_bytes, hipStream_t stream) {
   // Pairing pays off only when one 128-query tile per workgroup leaves CUs idle or runs a
   // single wave per SIMD anyway; larger grids keep the plain kernel (shared K/V stream, two
-  // waves per SIMD).
+  // waves per SIMD). Up to one tile pair per CU, d <= 64 takes the eight-wave split kernel;
+  // up to two, the four-wave paired kernel (two fit a CU), whose balanced steps beat the
+  // plain kernel's longest-tile tail.
   if constexpr (CAUSAL && D >= 32) {
-    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 128) * s.BH <= kNumCUs) {
-      const long long pairs = (long long)(s.Nq / 128) * s.BH;
+    const long long pairs = (long long)(s.Nq / 128) * s.BH;
+    if (D <= 64 && s.Nq == s.Nk && s.Nq % 128 == 0 && pairs > kNumCUs &&
+        pairs <= 2 * kNumCUs) {
+      hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
+                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
+                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+      return hipGetLastError();
+    }
+    if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs <= kNumCUs) {
       if constexpr (D <= 64) {
         int ns = fwd_split_ways(s);
         if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
@@ -1529,11 +1538,12 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   const float* L2 = ws;
   const float* ND = ws + rows;
   // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
-  // the longest tile on the critical path of a small grid; see bwd_causal_paired_kernel.
+  // the longest tile on the critical path of a small grid (up to three paired workgroups per
+  // CU, measured faster than the plain kernel there); see bwd_causal_paired_kernel.
   // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
   // instantiation, so it is not built.)
   if constexpr (CAUSAL && D >= 32 && D <= 64) {
-    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 2 * kNumCUs) {
+    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 3 * kNumCUs) {
       const long long wgs = (long long)(s.Nq / 64) * s.BH;
       // Partial sums for split grids follow the two per-row arrays in the workspace.
       int ns = bwd_split_ways(s);
