@@ -78,7 +78,7 @@ typedef enum fa_dtype {
  * fa_forward_workspace_bytes -- bytes of device workspace fa_forward can use for these
  * arguments (0 when it needs none, and for arguments fa_forward would reject).
  *
- * Small causal bf16 grids (Nq = Nk a multiple of 128, d = 32 or 64, few tiles per head)
+ * Small causal bf16 grids (Nq = Nk a multiple of 128, d = 32, 64 or 128, few tiles per head)
  * spread each pair of query tiles over several workgroups so that every CU has work; their
  * partial softmax states go to the workspace and a second launch merges them (the same
  * rescale the online softmax applies between key tiles, problem flash_forward). The size is

@@ -83,7 +83,9 @@ def test_forward_workspace_sizes(lib):
     assert ws(1, 1, 1, 8192, 8192, 32, 1) == 64 * 4 * 2 * 18 * 128 * 4
     assert ws(1, 8, 1, 4096, 4096, 64, 1) == 0      # 256 tile pairs fill the CUs already
     assert ws(1, 1, 1, 8192, 8192, 64, 0) == 0      # not causal
-    assert ws(1, 1, 1, 8192, 8192, 128, 1) == 0     # d = 128 is not split
+    # d = 128 (the paired kernel): 64 tile pairs x 4 ways x 2 records x 66 x 128 floats
+    assert ws(1, 1, 1, 8192, 8192, 128, 1) == 64 * 4 * 2 * 66 * 128 * 4
+    assert ws(1, 1, 1, 8192, 8192, 16, 1) == 0      # d = 16 is not split
     assert ws(1, 1, 1, 8192, 4096, 64, 1) == 0      # Nq != Nk
     assert ws(0, 1, 1, 8192, 8192, 64, 1) == 0      # fp32
     assert ws(1, 1, 1, 256, 256, 64, 1) == 0        # runs would be too short

@@ -253,6 +253,8 @@ SPLIT_WG = [
     (2, 3, 2048, 32),
     (1, 1, 4096, 32),
     (1, 2, 4096, 64),
+    (1, 2, 2048, 128),  # the paired forward kernel (d = 128), 4 ways
+    (1, 1, 4096, 128),  # 8 ways
 ]
 
 

@@ -320,7 +320,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
 template <int D>
 __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg) {
+    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg, int ns,
+    float* __restrict__ part) {
   constexpr int BK = 64;
   constexpr int DS = D / 16, DB = (D + 31) / 32;
   using KTile = Tile<BK, D>;
@@ -333,7 +334,8 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   const int T = N / 64;
   const int half = T / 2;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / half, i = lid % half;
+  const int sw = lid % ns, pid = lid / ns;  // this workgroup's share of tile pair pid
+  const int bh = pid / half, i = pid % half;
   const int tA = T - 1 - i, tB = i, s = half + 1;
   const rsrc_t Qr = make_rsrc(Q + (size_t)bh * N * D, (uint32_t)N * D * 2);
   const rsrc_t Kr = make_rsrc(K + (size_t)bh * N * D, (uint32_t)N * D * 2);
@@ -348,6 +350,12 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   //   pair 0: n in [0, s):           A, key tile n
   //   pair 1: n in [0, i+1):         B, key tile n;  n in [i+1, T-s+1): A, key tile n - (i+1) + s
   const int nsteps = pr == 0 ? s : T + 1 - s;
+  // With ns > 1 each pair runs only steps [n_lo, n_hi) of its sequence, and the workgroup
+  // writes partial (m, l, unnormalised O) records of A and B to `part` for
+  // fwd_split_combine_kernel (the layout of fwd_causal_split_kernel's records).
+  const int n_lo = sw * nsteps / ns, n_hi = (sw + 1) * nsteps / ns;
+  constexpr int XS = 16 * DB + 2;  // per lane: O block(s), m, l
+
   auto qt_of = [&](int n) { return (pr == 0 || n > tB) ? tA : tB; };
   auto kt_of = [&](int n) { return (pr == 0 || n <= tB) ? n : n - (tB + 1) + s; };
 
@@ -366,6 +374,27 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
   float m = 0.f, l = 0.f;
+  auto put_state = [&](bool tileA) {  // this wave's (m, l, O) as the share's record
+    float* x = part + ((size_t)pid * ns + sw) * 2 * (XS * 128) + (tileA ? 0 : XS * 128) +
+               wp * 64 + lane;
+    // Opaque here, so the store addresses are formed at the store (this runs once) rather
+    // than hoisted out of the step loop, where they would hold registers throughout.
+    asm volatile("" : "+v"(x));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[db][r];
+    x[16 * DB * 128] = m;
+    x[(16 * DB + 1) * 128] = l;
+  };
+  auto put_empty_B = [&]() {  // B's record from a share with no B step: m = -inf, l = O = 0
+    float* x = part + ((size_t)pid * ns + sw) * 2 * (XS * 128) + XS * 128 + wp * 64 + lane;
+    asm volatile("" : "+v"(x));
+#pragma unroll
+    for (int r = 0; r < 16 * DB; ++r) x[r * 128] = 0.f;
+    x[16 * DB * 128] = -INFINITY;
+    x[(16 * DB + 1) * 128] = 0.f;
+  };
 
   auto fetch = [&](int n, bf16 (*dst)[KT]) {
     const int k0 = kt_of(n) * BK;
@@ -373,10 +402,14 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
     KTile::template load<2>(Vr, k0, dst[1], wp, lane);
   };
   auto finish_B = [&]() {  // pair 1, after B's last key tile: B is complete
-    const float lt = halves_sum(l);
-    const int row = 64 * tB + 32 * wp + l32;
-    store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
-    if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
+    if (ns > 1) {
+      put_state(false);
+    } else {
+      const float lt = halves_sum(l);
+      const int row = 64 * tB + 32 * wp + l32;
+      store_rows_from_acc<D>(O + ((size_t)bh * N + row) * D, o, 1.f / lt, g);
+      if (g == 0) Lout[(size_t)bh * N + row] = m * cs + logf(lt);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16();
     m = 0.f;
@@ -388,7 +421,7 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
     // All of this step's LDS operands are requested up front, so the score MFMAs wait for the
     // first K fragment only (this kernel runs one wave per SIMD, so registers are plentiful).
     bf16x8 vfr[4][DB], kfr[2][DS];
-    if (n < nsteps) {
+    if (n < n_hi) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -398,11 +431,11 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 #pragma unroll
         for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(cur[0], 32 * kb + l32, 2 * q + g);
     }
-    if (n + 1 < nsteps) fetch(n + 1, nxt);
+    if (n + 1 < n_hi) fetch(n + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    if (n < nsteps) {
+    if (n < n_hi) {
       const int qt = qt_of(n), kt = kt_of(n);
-      const bool first = pr == 0 ? n == 0 : (n == 0 || n == tB + 1);
+      const bool first = n == n_lo || (pr == 1 && n == tB + 1);
       const int qrow = 64 * qt + 32 * wp + l32;
       const int k0 = kt * BK;
       const bf16x8(&qf)[DS] = qt == tA ? qfA : qfB;
@@ -427,17 +460,33 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
     __syncthreads();
   };
 
-  fetch(0, sb0[pr]);
+  // Both pairs step in lockstep over the longer of their two shares; a pair past the end of
+  // its share idles at the barriers.
+  const int len0 = (sw + 1) * s / ns - sw * s / ns;
+  const int len1 = (sw + 1) * (T + 1 - s) / ns - sw * (T + 1 - s) / ns;
+  const int len = len0 > len1 ? len0 : len1;
+  if (n_lo < n_hi) fetch(n_lo, sb0[pr]);
   wait_vmem();
   __syncthreads();
-  for (int n = 0; n < s; n += 2) {
-    step(n, sb0[pr], sb1[pr]);
-    if (n + 1 < s) step(n + 1, sb1[pr], sb0[pr]);
+  for (int j = 0; j < len; j += 2) {
+    step(n_lo + j, sb0[pr], sb1[pr]);
+    if (j + 1 < len) step(n_lo + j + 1, sb1[pr], sb0[pr]);
   }
 
-  // Merge A: pair 1 holds A over key tiles [s, T - i) unless that range is empty.
-  const bool p1_has_A = T - tB > s;
-  constexpr int XS = 16 * DB + 2;  // per lane: O block(s), m, l
+  // B's record when the share ends before B completes (pair 1's state is B's), or an empty
+  // one when the share has no B step (pair 1's state, if any, is then A's, kept for the merge).
+  if (ns > 1 && pr == 1) {
+    if (n_lo > tB || n_lo >= n_hi) {
+      put_empty_B();
+    } else if (n_hi <= tB) {
+      put_state(false);
+    }
+  }
+
+  // Merge A: pair 1 holds A over key tiles [s, T - i) unless its share has no A step. Both
+  // pairs decide this from pair 1's step range (n_lo and n_hi are each pair's own).
+  const int lo1 = sw * (T + 1 - s) / ns, hi1 = (sw + 1) * (T + 1 - s) / ns;
+  const bool p1_has_A = hi1 > (lo1 > tB + 1 ? lo1 : tB + 1);
   static_assert(2 * 64 * XS * sizeof(float) <= sizeof(sb0), "merge area must fit in sb0");
   // Component-major merge record (component k of wave wp's lane at k * 128 + wp * 64 + lane):
   // consecutive lanes write consecutive words, so the exchange is free of bank conflicts.
@@ -464,6 +513,10 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
         for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + x[(16 * db + r) * 128] * a1;
       l = l * a0 + l1 * a1;
       m = mm;
+    }
+    if (ns > 1) {
+      put_state(true);
+      return;
     }
     const float lt = halves_sum(l);
     const int row = 64 * tA + 32 * wp + l32;
@@ -1436,18 +1489,21 @@ int bwd_split_ways(const Shape& s) {
   return ns;
 }
 
-// Workgroups per tile pair of the causal split forward (d = 32, 64). Small grids spread each
-// pair's key steps over up to kMaxWays workgroups, doubling while the grid still fits the CUs
-// and every wave pair keeps a run of at least kMinRun key steps; larger grids use one.
+// Workgroups per tile pair of the causal small-grid forward kernels (the split kernel at
+// d = 32, 64; the paired kernel at d = 128). Small grids spread each pair's key steps over up
+// to kMaxWays workgroups, doubling while the grid still fits the CUs (one such workgroup per
+// CU) and every wave pair keeps a run of at least kMinRun key steps; larger grids use one.
 constexpr int kMinRun = 4, kMaxWays = 8;
 static_assert(kMaxWays <= 8, "fwd_split_combine_kernel merges at most 8 records per tile");
 int fwd_split_ways(const Shape& s) {
-  if (!s.causal || s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32 || s.d > 64) return 1;
+  if (!s.causal || s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32) return 1;
   const long long pairs = (long long)(s.Nq / 128) * s.BH;
   if (pairs > kNumCUs) return 1;
-  const int steps = s.Nq / 64 + 1, np = 4;  // key steps per tile pair, wave pairs per workgroup
+  // Key steps of one wave pair's run per share: the split kernel cuts the pair's T + 1 steps
+  // into 4 runs, the paired kernel's longer run is T/2 + 1.
+  const int steps = s.d <= 64 ? (s.Nq / 64 + 1) / 4 : s.Nq / 128 + 1;
   int ns = 1;
-  while (ns < kMaxWays && pairs * ns * 2 <= kNumCUs && steps / (np * ns * 2) >= kMinRun) ns *= 2;
+  while (ns < kMaxWays && pairs * ns * 2 <= kNumCUs && steps / (ns * 2) >= kMinRun) ns *= 2;
   return ns;
 }
 
@@ -1483,29 +1539,30 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
         pairs <= 2 * kNumCUs) {
       hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
                          stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0, 1, nullptr);
       return hipGetLastError();
     }
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs <= kNumCUs) {
-      if constexpr (D <= 64) {
-        int ns = fwd_split_ways(s);
-        if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
+      int ns = fwd_split_ways(s);
+      if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
+      if constexpr (D <= 64)
         hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3((unsigned)(pairs * ns)),
                            dim3(512), 0, stream, (const bf16*)Q, (const bf16*)K,
                            (const bf16*)V, (bf16*)O, L, s.Nq, s.scale, s.scale < 0.f ? 1 : 0,
                            ns, ws);
-        if (ns > 1) {
-          const hipError_t e = hipGetLastError();
-          if (e != hipSuccess) return e;
-          hipLaunchKernelGGL((fwd_split_combine_kernel<D>),
-                             dim3((unsigned)((long long)s.BH * (s.Nq / 64))),
-                             dim3(128 * ((D + 31) / 32)), 0,
-                             stream, (const float*)ws, (bf16*)O, L, s.Nq, s.scale, ns);
-        }
-      } else
-        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
-                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0);
+      else
+        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)(pairs * ns)),
+                           dim3(256), 0, stream, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, (bf16*)O, L, s.Nq, s.scale, s.scale < 0.f ? 1 : 0,
+                           ns, ws);
+      if (ns > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((fwd_split_combine_kernel<D>),
+                           dim3((unsigned)((long long)s.BH * (s.Nq / 64))),
+                           dim3(128 * ((D + 31) / 32)), 0, stream, (const float*)ws, (bf16*)O,
+                           L, s.Nq, s.scale, ns);
+      }
       return hipGetLastError();
     }
   }
