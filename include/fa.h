@@ -78,7 +78,7 @@ typedef enum fa_dtype {
  * fa_forward_workspace_bytes -- bytes of device workspace fa_forward can use for these
  * arguments (0 when it needs none, and for arguments fa_forward would reject).
  *
- * Small causal bf16 grids (Nq = Nk a multiple of 128, d = 32, 64 or 128, few tiles per head)
+ * Small causal bf16 grids (Nq = Nk a multiple of 128, any d, few tiles per head)
  * spread each pair of query tiles over several workgroups so that every CU has work; their
  * partial softmax states go to the workspace and a second launch merges them (the same
  * rescale the online softmax applies between key tiles, problem flash_forward). The size is
@@ -121,12 +121,12 @@ FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, in
  * sizes (for fp32, and for sizes fa_backward would reject, 0). For bf16 it is
  *   - two floats per query row (B * H * Nq * 8 bytes, the minimum fa_backward accepts): the
  *     preprocessing step's per-row terms L log2(e) and -D, at the start of the workspace;
- *   - plus, for small square grids (Nq = Nk a multiple of 128, d = 32 or 64, at most 512
- *     64-row tiles), room for fp32 partial sums: a causal call then spreads each
- *     workgroup's steps over several workgroups and a second launch adds the partial dQ, dK
- *     and dV up ((Nq/64) * B * H * ways * 48 * ceil(d/32) * 128 * 4 bytes, ways in {2, 4, 8}).
- *     With only the minimum, those calls run one workgroup per tile pair (slower; results
- *     differ only in the order of the final additions).
+ *   - plus, for small square grids (Nq = Nk a multiple of 128, at most 1024 64-row tiles),
+ *     room for fp32 partial sums: the call then spreads each workgroup's steps over several
+ *     workgroups and a second launch adds the partial dQ, dK and dV up
+ *     ((Nq/64) * B * H * ways * 3 * 64 * d * 4 bytes, ways in {2, 4, 8}; the larger of the
+ *     causal and the non-causal call's ways). With only the minimum, those calls run one
+ *     workgroup per tile (slower; results differ only in the order of the final additions).
  * The caller owns the workspace; its contents need no initialisation and are meaningless
  * after the call.
  */

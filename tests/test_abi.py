@@ -64,9 +64,14 @@ def test_workspace_sizes(lib):
     # floats x 128 lanes (B*H = 1, N = 8192, d = 64: 128 tiles, 4 ways).
     assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 64) == (
         8192 * 8 + 128 * 4 * 96 * 128 * 4)
+    # N = 2048, d = 32: the causal paired kernel takes 4 ways, the non-causal bwd_kernel 8 (its
+    # steps are 32 rows); the size covers either.
     assert lib.fa_backward_workspace_bytes(1, 1, 1, 2048, 2048, 32) == (
-        2048 * 8 + 32 * 4 * 48 * 128 * 4)
-    assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 128) == 8192 * 8
+        2048 * 8 + 32 * 8 * 48 * 128 * 4)
+    # d = 128 (bwd_kernel, one workgroup per CU): causal 4 ways, non-causal 2.
+    assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 128) == (
+        8192 * 8 + 128 * 4 * 192 * 128 * 4)
+    assert lib.fa_backward_workspace_bytes(1, 8, 1, 8192, 8192, 128) == 8 * 8192 * 8
     assert lib.fa_backward_workspace_bytes(1, 4, 25, 2048, 1024, 128) == 100 * 2048 * 8
     assert lib.fa_backward_workspace_bytes(1, 2, 3, 0, 64, 64) == 0
     assert lib.fa_backward_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 0
@@ -85,7 +90,7 @@ def test_forward_workspace_sizes(lib):
     assert ws(1, 1, 1, 8192, 8192, 64, 0) == 0      # not causal
     # d = 128 (the paired kernel): 64 tile pairs x 4 ways x 2 records x 66 x 128 floats
     assert ws(1, 1, 1, 8192, 8192, 128, 1) == 64 * 4 * 2 * 66 * 128 * 4
-    assert ws(1, 1, 1, 8192, 8192, 16, 1) == 0      # d = 16 is not split
+    assert ws(1, 1, 1, 8192, 8192, 16, 1) == 64 * 4 * 2 * 18 * 128 * 4  # split kernel, d = 16
     assert ws(1, 1, 1, 8192, 4096, 64, 1) == 0      # Nq != Nk
     assert ws(0, 1, 1, 8192, 8192, 64, 1) == 0      # fp32
     assert ws(1, 1, 1, 256, 256, 64, 1) == 0        # runs would be too short

@@ -255,6 +255,8 @@ SPLIT_WG = [
     (1, 2, 4096, 64),
     (1, 2, 2048, 128),  # the paired forward kernel (d = 128), 4 ways
     (1, 1, 4096, 128),  # 8 ways
+    (1, 1, 4096, 16),   # the split kernel at d = 16 (padded LDS slots), 4 ways
+    (2, 1, 2048, 16),   # 2 ways
 ]
 
 
@@ -288,16 +290,44 @@ def test_mid_grids_take_paired_kernels(gpu, case):
     compare(got, full_oracle(inp, True, scale, heads), "bf16", heads)
 
 
-def test_backward_minimum_workspace_matches_split(gpu):
+# Small backward grids of bwd_kernel (d = 16 and 128, and every non-causal grid): each
+# workgroup's steps spread over several workgroups, whose fp32 partial sums a second launch adds.
+SPLIT_BWD = [
+    (1, 1, 2048, 16, True),
+    (1, 2, 2048, 128, True),
+    (1, 1, 4096, 128, True),
+    (1, 1, 2048, 64, False),
+    (2, 1, 1024, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_BWD, ids=lambda c: "B{}H{}N{}d{}{}".format(
+    *c[:4], "causal" if c[4] else "full"))
+def test_backward_split_over_workgroups_matches_oracle(gpu, case):
+    from tiled_attention_causal_amd import backward_workspace_bytes
+    B, H, N, d, causal = case
+    note(f"split backward case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=9300 + N + d + H + causal)
+    assert backward_workspace_bytes(inp["q"], inp["k"]) > B * H * N * 8
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, causal, scale, gpu)
+    heads = [(0, 0), (B - 1, H - 1)]
+    compare(got, full_oracle(inp, causal, scale, heads), "bf16", heads)
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, True), (64, False)])
+def test_backward_minimum_workspace_matches_split(gpu, d, causal):
     """A workspace of only the per-row terms: the same grid runs unsplit, which changes only
     the order of the partial-sum additions."""
     from tiled_attention_causal_amd import backward_workspace_bytes, fa_backward, fa_forward
-    inp = make_inputs(1, 2, 4096, 4096, 64, "bf16", index=8900)
+    note(f"minimum backward workspace d={d} causal={causal}")
+    inp = make_inputs(1, 2, 4096, 4096, d, "bf16", index=8900 + d + causal)
     q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
     assert backward_workspace_bytes(q, k) > 2 * 4096 * 8
-    o, lse = fa_forward(q, k, v, True, 0.125)
-    g1 = fa_backward(q, k, v, o, lse, do, True, 0.125)
-    g2 = fa_backward(q, k, v, o, lse, do, True, 0.125,
+    sc = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = fa_forward(q, k, v, causal, sc)
+    g1 = fa_backward(q, k, v, o, lse, do, causal, sc)
+    g2 = fa_backward(q, k, v, o, lse, do, causal, sc,
                      workspace=torch.empty(2 * 4096 * 8, dtype=torch.uint8, device=gpu))
     torch.cuda.synchronize(gpu)
     for a, b in zip(g1, g2):

@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   }
 }
 
-// Causal forward for Nq = Nk = N, N % 128 == 0, 32 <= d <= 64, on eight waves (two per SIMD).
+// Causal forward for Nq = Nk = N, N % 128 == 0, d <= 64, on eight waves (two per SIMD).
 //
 // As in fwd_causal_paired_kernel, workgroup i takes the 64-row query tiles A = T-1-i and
 // B = i (T = N/64), which need T + 1 key steps together: A over key tiles 0 .. T-i-1, then
@@ -545,7 +545,11 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   using KTile = Tile<BK, D>;
   constexpr int KT = KTile::ELEMS;
   constexpr int XS = 16 * DB + 2;  // parked partial: O registers, m, l (component-major)
-  __shared__ __attribute__((aligned(1024))) bf16 kv[NP][2][2][KT];  // [pair][buffer][K | V]
+  // K/V slots, padded where the parked partials need more room than the tiles (d = 16; the
+  // pad keeps every slot at a multiple of 256 bytes, so the bank mapping is unchanged).
+  constexpr int KTS = KT > 64 * XS ? KT : 64 * XS;
+  static_assert(KTS * 2 % 256 == 0, "K/V slots must keep the bank mapping");
+  __shared__ __attribute__((aligned(1024))) bf16 kv[NP][2][2][KTS];  // [pair][buffer][K | V]
   __shared__ __attribute__((aligned(16))) float park_cross[XS * 128];
   static_assert(NP * XS * 128 * sizeof(float) <= sizeof(kv), "parked partials must fit in kv");
 
@@ -762,6 +766,7 @@ __global__ __launch_bounds__(128 * ((D + 31) / 32)) void fwd_split_combine_kerne
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int d0 = 32 * db + 8 * j + 4 * g;
+    if (d0 >= D) continue;  // d = 16: half of the block is padding
     bf16x4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[4 * j + e] * inv);
@@ -1024,12 +1029,43 @@ __device__ __forceinline__ void load_kv_rows(bf16x8 (&kf)[D / 16], bf16x8 (&vf)[
     for (int s = 0; s < D / 16; ++s) kf[s] = negate(kf[s]);
 }
 
-// dK, dV for the 128 keys starting at k0 of one head (4 waves share one query stream).
+// Partial sums of the split backward: an accumulator set stored unscaled as fp32 rows, the
+// layout store_rows_from_acc gives bf16 outputs (lane owns row `out_row`; register r of block
+// db holds column 32db + 8(r/4) + 4g + r%4), or zeros for a share with no step of the tile.
+template <int D>
+__device__ __forceinline__ void put_rows_f32(float* out_row, const f32x16 (&acc)[(D + 31) / 32],
+                                             int g) {
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (32 * db + 8 * j + 4 * g >= D) continue;  // d = 16: half of the block is padding
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = acc[db][4 * j + i];
+      *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = v;
+    }
+}
+template <int D>
+__device__ __forceinline__ void put_zero_rows_f32(float* out_row, int g) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (32 * db + 8 * j + 4 * g < D)
+        *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = z;
+}
+
+// dK, dV for the 128 keys starting at k0 of one head (4 waves share one query stream). With
+// ns > 1 this is share sw of the query steps, and the sums go unscaled to the fp32 partial
+// tiles of the head at `part` (see bwd_kernel) instead of dK and dV.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr,
                                           rsrc_t L2r, rsrc_t NDr, rsrc_t dOr, bf16* dKh,
                                           bf16* dVh, int k0,
-                                          int Nq, int Nk, float scale, int neg) {
+                                          int Nq, int Nk, float scale, int neg, int sw, int ns,
+                                          float* part) {
   using B = Bwd<D>;
   constexpr int DS = B::DS, DB = B::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
@@ -1047,17 +1083,18 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   }
 
   const int nmt = (Nq + 31) / 32;
-  const int mt0 = CAUSAL ? k0 / 32 : 0;
-  if (mt0 < nmt) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, mt0 * 32, smem, w, lane);
+  const int mt0 = CAUSAL ? min(k0 / 32, nmt) : 0;
+  const int lo = mt0 + sw * (nmt - mt0) / ns, hi = mt0 + (sw + 1) * (nmt - mt0) / ns;
+  if (lo < hi) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, lo * 32, smem, w, lane);
   wait_vmem();
   __syncthreads();
-  for (int mt = mt0; mt < nmt; ++mt) {
-    bf16* buf = smem + ((mt - mt0) & 1) * B::KV_BUF;
-    bf16* nbuf = smem + (((mt - mt0) & 1) ^ 1) * B::KV_BUF;
+  for (int mt = lo; mt < hi; ++mt) {
+    bf16* buf = smem + ((mt - lo) & 1) * B::KV_BUF;
+    bf16* nbuf = smem + (((mt - lo) & 1) ^ 1) * B::KV_BUF;
     const int m0 = mt * 32;
     const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
     KvOps<D> op;  // unused: transposed operands are read late (see KvOps)
-    if (mt + 1 < nmt) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, m0 + 32, nbuf, w, lane);
+    if (mt + 1 < hi) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, m0 + 32, nbuf, w, lane);
     if (active)
       kv_step<D, false>(buf, op, kf, vf, dvt, dkt, c, CAUSAL && m0 < kw0 + 31,
                         krow - m0 - 4 * g, lane, l32, g);
@@ -1065,18 +1102,24 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
     __syncthreads();
   }
 
-  if (krow < Nk) {
+  if (ns > 1) {  // Nq = Nk, a multiple of 128: every row exists
+    float* x = part + (((size_t)(krow / 64) * ns + sw) * 2 * 64 + krow % 64) * D;
+    asm volatile("" : "+v"(x));  // address formed here, not held through the loop
+    put_rows_f32<D>(x, dkt, g);
+    put_rows_f32<D>(x + 64 * D, dvt, g);
+  } else if (krow < Nk) {
     store_rows_from_acc<D>(dKh + (size_t)krow * D, dkt, scale, g);
     store_rows_from_acc<D>(dVh + (size_t)krow * D, dvt, 1.f, g);
   }
 }
 
-// dQ for the 128 queries starting at q0 of one head (4 waves share one key stream).
+// dQ for the 128 queries starting at q0 of one head (4 waves share one key stream). With
+// ns > 1 this is share sw of the key steps, summed into the head's fp32 partial tiles at `part`.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr,
                                         rsrc_t L2r, rsrc_t NDr, rsrc_t dOr, bf16* dQh, int q0,
                                         int Nq, int Nk,
-                                        float scale, int neg) {
+                                        float scale, int neg, int sw, int ns, float* part) {
   using B = Bwd<D>;
   constexpr int DB = B::DB;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
@@ -1092,19 +1135,20 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
 
   int nkt = (Nk + 31) / 32;
   if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / 32 + 1);
-  if (nkt > 0) {
-    B::MTile::template load<4>(Kr, 0, smem, w, lane);
-    B::MTile::template load<4>(Vr, 0, smem + B::T, w, lane);
+  const int lo = sw * nkt / ns, hi = (sw + 1) * nkt / ns;
+  if (lo < hi) {
+    B::MTile::template load<4>(Kr, lo * 32, smem, w, lane);
+    B::MTile::template load<4>(Vr, lo * 32, smem + B::T, w, lane);
   }
   wait_vmem();
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bf16* buf = smem + (kt & 1) * B::Q_BUF;
-    bf16* nbuf = smem + ((kt & 1) ^ 1) * B::Q_BUF;
+  for (int kt = lo; kt < hi; ++kt) {
+    const bf16* buf = smem + ((kt - lo) & 1) * B::Q_BUF;
+    bf16* nbuf = smem + (((kt - lo) & 1) ^ 1) * B::Q_BUF;
     const int n0 = kt * 32;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
     QOps<D> op;  // unused: transposed operands are read late (see KvOps)
-    if (kt + 1 < nkt) {
+    if (kt + 1 < hi) {
       B::MTile::template load<4>(Kr, n0 + 32, nbuf, w, lane);
       B::MTile::template load<4>(Vr, n0 + 32, nbuf + B::T, w, lane);
     }
@@ -1117,12 +1161,24 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
     __syncthreads();
   }
 
-  if (qrow < Nq) store_rows_from_acc<D>(dQh + (size_t)qrow * D, dqt, scale, g);
+  if (ns > 1) {
+    float* x = part + ((size_t)(qrow / 64) * ns + sw) * 64 * D + (size_t)(qrow % 64) * D;
+    asm volatile("" : "+v"(x));
+    put_rows_f32<D>(x, dqt, g);
+  } else if (qrow < Nq) {
+    store_rows_from_acc<D>(dQh + (size_t)qrow * D, dqt, scale, g);
+  }
 }
 
 // One launch for the whole backward. Per head the workgroups run the dK/dV key tiles first
 // and then the dQ query tiles, each kind longest first: the dK/dV tiles that finish first
 // (few visible queries) free their CUs for the longest dQ tiles.
+//
+// Small grids (Nq = Nk = N, N % 128 == 0) spread each workgroup's steps over ns workgroups
+// (consecutive blocks, so a tile's shares start together): share sw runs the sw-th of ns equal
+// slices and writes fp32 partial sums, per 64-row tile t of head bh and share sw, as [64][D]
+// rows of dK^T and dV^T at kvpart + ((bh T + t) ns + sw) 2 * 64 D (dV^T after dK^T) and of dQ^T
+// at qpart + ((bh T + t) ns + sw) 64 D, T = N / 64; bwd_split_combine_kernel adds them up.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
@@ -1132,13 +1188,20 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
                                                   const bf16* __restrict__ dO,
                                                   bf16* __restrict__ dQ, bf16* __restrict__ dK,
                                                   bf16* __restrict__ dV, int Nq, int Nk,
-                                                  float scale, int neg) {
+                                                  float scale, int neg, int ns,
+                                                  float* __restrict__ kvpart,
+                                                  float* __restrict__ qpart) {
   constexpr int SM = Bwd<D>::KV_BUF > Bwd<D>::Q_BUF ? Bwd<D>::KV_BUF : Bwd<D>::Q_BUF;
   __shared__ __attribute__((aligned(1024))) bf16 smem[2 * SM];
   const int nkv = (Nk + 127) / 128, nqw = (Nq + 127) / 128;
   const int per_head = nkv + nqw;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / per_head, idx = lid % per_head;
+  // Split grids keep the dispatch order: the hardware deals consecutive blocks to the eight
+  // XCDs in turn, so every XCD gets its even share of the long and the short shares (by
+  // XCD-contiguous ranges one XCD would take all the longest dK/dV tiles of a head).
+  const int lid = ns > 1 ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int sw = lid % ns, pid = lid / ns;
+  const int bh = pid / per_head, idx = pid % per_head;
+  const size_t head_part = (size_t)bh * (Nq / 64) * ns * 64 * D;  // one tensor's tiles per head
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
   const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
   const rsrc_t Qr = make_rsrc(Q + oq, bq), dOr = make_rsrc(dO + oq, bq);
@@ -1147,10 +1210,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* _
   const rsrc_t NDr = make_rsrc(ND + (size_t)bh * Nq, (uint32_t)Nq * 4);
   if (idx < nkv) {
     dkdv_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dK + ok, dV + ok, idx * 128, Nq, Nk,
-                         scale, neg);
+                         scale, neg, sw, ns, ns > 1 ? kvpart + 2 * head_part : nullptr);
   } else {
     const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
-    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg);
+    dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg,
+                       sw, ns, ns > 1 ? qpart + head_part : nullptr);
   }
 }
 
@@ -1186,31 +1250,6 @@ __device__ __forceinline__ void stream3(int first, int last, bf16* __restrict__ 
     if (n + 1 < last) one(n + 1, b1, b0);
     if (n + 2 < last) one(n + 2, b2, b1);
   }
-}
-
-// Partial sums of the split backward: an accumulator set stored unscaled as fp32 rows, the
-// layout store_rows_from_acc gives bf16 outputs (lane owns row `out_row`; register r of block
-// db holds column 32db + 8(r/4) + 4g + r%4), or zeros for a share with no step of the tile.
-template <int D>
-__device__ __forceinline__ void put_rows_f32(float* out_row, const f32x16 (&acc)[(D + 31) / 32],
-                                             int g) {
-#pragma unroll
-  for (int db = 0; db < (D + 31) / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[db][4 * j + i];
-      *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = v;
-    }
-}
-template <int D>
-__device__ __forceinline__ void put_zero_rows_f32(float* out_row, int g) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int db = 0; db < (D + 31) / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(out_row + 32 * db + 8 * j + 4 * g) = z;
 }
 
 // Causal backward with complementary tile pairing, for Nq = Nk = N, N % 128 == 0 (the
@@ -1440,11 +1479,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
   }
 }
 
-// Adds the ns partial [64][D] fp32 tiles bwd_causal_paired_kernel wrote for each 64-row tile
-// when it spreads every workgroup's steps over ns workgroups, scales dK and dQ, and stores
-// dQ, dK and dV. Each thread sums one float4 of one tensor over the ns shares (independent
-// loads, consecutive threads on consecutive addresses); a tile's three tensors take
-// 3 * 64 * D / 1024 workgroups of 256 threads.
+// Adds the ns partial [64][D] fp32 tiles that bwd_causal_paired_kernel or bwd_kernel wrote for
+// each 64-row tile when it spread every workgroup's steps over ns workgroups, scales dK and dQ,
+// and stores dQ, dK and dV. Each thread sums one float4 of one tensor over the ns shares
+// (independent loads, consecutive threads on consecutive addresses); a tile's three tensors
+// take 3 * 64 * D / 1024 workgroups of 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_split_combine_kernel(
     const float* __restrict__ kvpart, const float* __restrict__ qpart, bf16* __restrict__ dQ,
@@ -1475,28 +1514,39 @@ __global__ __launch_bounds__(256) void bwd_split_combine_kernel(
   *reinterpret_cast<bf16x4*>(out + ((size_t)bh * N + 64 * tile) * D + k) = o;
 }
 
-// Workgroups per workgroup of the causal paired backward (d = 32, 64): small grids spread each
-// workgroup's T+1 steps over up to kMaxWays workgroups, doubling while the grid stays within
-// two workgroups per CU and every share keeps at least kMinShare steps.
+// The causal paired backward runs grids of up to three of its workgroups per CU (d = 32, 64).
+bool bwd_uses_paired(const Shape& s) {
+  return s.causal && s.d >= 32 && s.d <= 64 && s.Nq == s.Nk && s.Nq % 128 == 0 &&
+         (long long)(s.Nq / 64) * s.BH <= 3 * kNumCUs;
+}
+
+// Workgroups per workgroup of the split backward (Nq = Nk, a multiple of 128). Small grids
+// spread each workgroup's steps over up to 8 workgroups, doubling while every share keeps at
+// least kMinShare steps and the grid stays within the CUs' room for the kernel's workgroups
+// (two per CU for the paired kernel and bwd_kernel at d <= 64, one for bwd_kernel at d = 128).
+// Causal bwd_kernel grids may take twice that: their shares differ in length, and dispatched
+// longest first, the short dK/dV shares free their CUs for the long dQ ones.
 constexpr int kMinShare = 8;
 int bwd_split_ways(const Shape& s) {
-  if (s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32 || s.d > 64) return 1;
-  const long long wgs = (long long)(s.Nq / 64) * s.BH;
-  if (wgs > 2 * kNumCUs) return 1;
-  const int steps = s.Nq / 64 + 1;
+  if (s.Nq != s.Nk || s.Nq % 128 != 0) return 1;
+  const bool paired = bwd_uses_paired(s);
+  const long long wgs = (long long)(s.Nq / 64) * s.BH;  // either kernel: N / 64 per head
+  const long long room = (long long)kNumCUs * (paired || s.d <= 64 ? 2 : 1) *
+                         (!paired && s.causal ? 2 : 1);
+  const int steps = paired ? s.Nq / 64 + 1 : s.Nq / 32;  // the longest workgroup's steps
   int ns = 1;
-  while (ns < 8 && wgs * ns * 2 <= 2 * kNumCUs && steps / (ns * 2) >= kMinShare) ns *= 2;
+  while (ns < 8 && wgs * ns * 2 <= room && steps / (ns * 2) >= kMinShare) ns *= 2;
   return ns;
 }
 
 // Workgroups per tile pair of the causal small-grid forward kernels (the split kernel at
-// d = 32, 64; the paired kernel at d = 128). Small grids spread each pair's key steps over up
+// d <= 64; the paired kernel at d = 128). Small grids spread each pair's key steps over up
 // to kMaxWays workgroups, doubling while the grid still fits the CUs (one such workgroup per
 // CU) and every wave pair keeps a run of at least kMinRun key steps; larger grids use one.
 constexpr int kMinRun = 4, kMaxWays = 8;
 static_assert(kMaxWays <= 8, "fwd_split_combine_kernel merges at most 8 records per tile");
 int fwd_split_ways(const Shape& s) {
-  if (!s.causal || s.Nq != s.Nk || s.Nq % 128 != 0 || s.d < 32) return 1;
+  if (!s.causal || s.Nq != s.Nk || s.Nq % 128 != 0) return 1;
   const long long pairs = (long long)(s.Nq / 128) * s.BH;
   if (pairs > kNumCUs) return 1;
   // Key steps of one wave pair's run per share: the split kernel cuts the pair's T + 1 steps
@@ -1517,7 +1567,11 @@ size_t fwd_workspace_bytes_bf16(const Shape& s) {
 }
 
 size_t bwd_split_workspace_bytes_bf16(const Shape& s) {
-  const int ns = bwd_split_ways(s);
+  // The size does not depend on the call being causal: room for either.
+  Shape c = s, n = s;
+  c.causal = true;
+  n.causal = false;
+  const int ns = std::max(bwd_split_ways(c), bwd_split_ways(n));
   if (ns == 1) return 0;
   // Per 64-row tile and share: fp32 [64][d] tiles of dK^T, dV^T and dQ^T.
   return (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
@@ -1531,16 +1585,17 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
   // Pairing pays off only when one 128-query tile per workgroup leaves CUs idle or runs a
   // single wave per SIMD anyway; larger grids keep the plain kernel (shared K/V stream, two
   // waves per SIMD). Up to one tile pair per CU, d <= 64 takes the eight-wave split kernel;
-  // up to two, the four-wave paired kernel (two fit a CU), whose balanced steps beat the
-  // plain kernel's longest-tile tail.
-  if constexpr (CAUSAL && D >= 32) {
+  // up to two (d = 32, 64), the four-wave paired kernel (two fit a CU), whose balanced steps
+  // beat the plain kernel's longest-tile tail.
+  if constexpr (CAUSAL) {
     const long long pairs = (long long)(s.Nq / 128) * s.BH;
-    if (D <= 64 && s.Nq == s.Nk && s.Nq % 128 == 0 && pairs > kNumCUs &&
-        pairs <= 2 * kNumCUs) {
-      hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
-                         stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                         s.Nq, s.scale, s.scale < 0.f ? 1 : 0, 1, nullptr);
-      return hipGetLastError();
+    if constexpr (D >= 32 && D <= 64) {
+      if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs > kNumCUs && pairs <= 2 * kNumCUs) {
+        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
+                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
+                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0, 1, nullptr);
+        return hipGetLastError();
+      }
     }
     if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs <= kNumCUs) {
       int ns = fwd_split_ways(s);
@@ -1594,42 +1649,44 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   const long long rows = (long long)s.BH * s.Nq;
   const float* L2 = ws;
   const float* ND = ws + rows;
+  // Partial sums of split grids follow the two per-row arrays in the workspace.
+  int ns = bwd_split_ways(s);
+  const size_t split_bytes = (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * D * sizeof(float);
+  if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes ||
+                 (reinterpret_cast<uintptr_t>(ws) & 15u) != 0))
+    ns = 1;  // the partial tiles are written and read 16 bytes at a time
+  const long long tiles = (long long)(s.Nq / 64) * s.BH;  // 64-row tiles (when ns > 1)
+  float* kvpart = const_cast<float*>(ws) + 2 * rows;
+  float* qpart = kvpart + (size_t)tiles * ns * 2 * 64 * D;  // after dK^T, dV^T of every tile
+  bool launched = false;
   // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
   // the longest tile on the critical path of a small grid (up to three paired workgroups per
   // CU, measured faster than the plain kernel there); see bwd_causal_paired_kernel.
   // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
   // instantiation, so it is not built.)
   if constexpr (CAUSAL && D >= 32 && D <= 64) {
-    if (s.Nq == s.Nk && s.Nq % 128 == 0 && (long long)(s.Nq / 64) * s.BH <= 3 * kNumCUs) {
-      const long long wgs = (long long)(s.Nq / 64) * s.BH;
-      // Partial sums for split grids follow the two per-row arrays in the workspace.
-      int ns = bwd_split_ways(s);
-      const size_t split_bytes = bwd_split_workspace_bytes_bf16(s);
-      if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes ||
-                     (reinterpret_cast<uintptr_t>(ws) & 15u) != 0))
-        ns = 1;  // the partial tiles are written and read 16 bytes at a time
-      float* kvpart = const_cast<float*>(ws) + 2 * rows;
-      float* qpart = kvpart + (size_t)wgs * ns * 2 * 64 * D;  // after dK^T, dV^T of every tile
-      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(wgs * ns)), dim3(256),
+    if (bwd_uses_paired(s)) {
+      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(tiles * ns)), dim3(256),
                          0, stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
                          (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
                          s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
-      if (ns > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_split_combine_kernel<D>),
-                           dim3((unsigned)(wgs * (3 * 64 * D / 1024))), dim3(256), 0, stream,
-                           (const float*)kvpart,
-                           (const float*)qpart, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
-                           ns);
-      }
-      return hipGetLastError();
+      launched = true;
     }
   }
-  const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH;
-  hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND, (const bf16*)dO,
-                     (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.Nk, s.scale, s.scale < 0.f ? 1 : 0);
+  if (!launched) {
+    const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH * ns;
+    hipLaunchKernelGGL((bwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND, (const bf16*)dO,
+                       (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.Nk, s.scale,
+                       s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
+  }
+  if (ns > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_split_combine_kernel<D>), dim3((unsigned)(tiles * (3 * 64 * D / 1024))),
+                       dim3(256), 0, stream, (const float*)kvpart, (const float*)qpart, (bf16*)dQ,
+                       (bf16*)dK, (bf16*)dV, s.Nq, s.scale, ns);
+  }
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const v
 // per-row terms (L log2(e) and -D) from O, L and dO, the second reads them.
 hipError_t launch_bwd_prep_bf16(const Shape& s, const void* O, const float* L, const void* dO,
                                 float* workspace, hipStream_t stream);
-// Small causal grids (Nq = Nk, d = 32 or 64) spread each workgroup's steps over several
+// Small square grids (Nq = Nk, a multiple of 128) spread each workgroup's steps over several
 // workgroups when the workspace also holds bwd_split_workspace_bytes_bf16 bytes of fp32 partial
 // sums after the per-row terms; a second launch adds them up.
 size_t bwd_split_workspace_bytes_bf16(const Shape& s);
