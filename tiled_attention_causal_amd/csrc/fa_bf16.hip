@@ -31,98 +31,11 @@ namespace {
 
 constexpr int kNumCUs = 256;  // MI355X
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   u32x4 u = __builtin_bit_cast(u32x4, x);
   u ^= 0x80008000u;
   return __builtin_bit_cast(bf16x8, u);
 }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// scale * log2(e) for the exponentials, floored at 1e-30 so that masked scores, set to -inf,
-// give exp2(-inf * c) = 0 even for scale = 0. With c = 1e-30 every visible exponent is below
-// 2^-80 in magnitude, whose exp2 rounds to exactly 1 in fp32: the same P as c = 0.
-__device__ __forceinline__ float exp2_coef(float scale) {
-  return fmaxf(fabsf(scale) * kLog2e, 1e-30f);
-}
-
-// Set score registers whose offset 8(r/4) + r%4 (+32 per block) is not visible to -inf:
-// visible iff lo <= offset <= hi.
-template <int NBLK>
-__device__ __forceinline__ void mask_scores(f32x16 (&s)[NBLK], int lo, int hi) {
-#pragma unroll
-  for (int kb = 0; kb < NBLK; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-      if (off < lo || off > hi) s[kb][r] = -INFINITY;
-    }
-}
-
-// Wave index as a scalar, so LDS destinations of the direct loads stay uniform.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at dst + 16 i.
-__device__ __forceinline__ void dma16(rsrc_t src, uint32_t byte_off, void* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 16, byte_off, 0, 0, 0);
-}
-// 4 bytes per lane (lane i's word lands at dst + 4 i).
-__device__ __forceinline__ void dma4(rsrc_t src, uint32_t byte_off, void* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 4, byte_off, 0, 0, 0);
-}
-
-// Row-major R x C bf16 LDS tile with 16-byte chunks XOR-swizzled by row (swz in fa_common.h).
-template <int R, int C>
-struct Tile {
-  static constexpr int NCH = C / 8;
-  static constexpr int ELEMS = R * C;
-  static constexpr int NKIB = ELEMS * 2 / 1024;  // one wave-wide direct load moves 1 KiB
-  static_assert(ELEMS * 2 % 1024 == 0, "tile must be a whole number of KiB");
-
-  // Rows [row0, row0 + R) of a head with C columns, spread over NW waves. LDS chunk p holds
-  // the global chunk whose swizzled position is p; rows past the head's end read as zeros.
-  template <int NW>
-  __device__ __forceinline__ static void load(rsrc_t src, int row0, bf16* t, int w, int lane) {
-#pragma unroll
-    for (int i = 0; i < (NKIB + NW - 1) / NW; ++i) {
-      const int blk = w + i * NW;
-      if (NKIB % NW == 0 || blk < NKIB) {
-        const int p = blk * 64 + lane;
-        const int row = p / NCH, cp = p % NCH;
-        const int gc = cp ^ swz_key<NCH>(row);
-        dma16(src, (uint32_t)(((row0 + row) * C + gc * 8) * 2), t + blk * 512);
-      }
-    }
-  }
-  // Operand with k along columns: lane takes row r, columns 8c .. 8c+7.
-  __device__ __forceinline__ static bf16x8 frag(const bf16* t, int r, int c) {
-    return lds_frag<NCH>(t, r, c);
-  }
-  // Transposed operand: lane l takes column cbase + l%32 and the eight rows
-  // kbase + 8h + 4g + j (h = 0, 1; j = 0..3; g = l/32) in element order 4h + j, which is the
-  // row order of an MFMA C fragment's 16-row step. Each ds_read_b64_tr_b16 gathers, inside
-  // a 16-lane group, the 4 x 4 block that lane 4a + b's column needs: lane k of the group
-  // reads row base + k/4, columns 4(k%4) .. +3, and receives column 4a+b of rows base..+3.
-  __device__ __forceinline__ static bf16x8 tfrag(const bf16* t, int cbase, int kbase, int lane) {
-    const int g = lane >> 5, s = (lane >> 4) & 1, k = lane & 15;
-    int col = cbase + 16 * s + 4 * (k & 3);
-    if constexpr (C < 32) col &= C - 1;  // d = 16: the unused half-block re-reads valid columns
-    const int row = kbase + 4 * g + (k >> 2);
-    const bf16* p0 = t + swz<NCH>(row, col >> 3) + (col & 7);
-    const bf16* p1 = t + swz<NCH>(row + 8, col >> 3) + (col & 7);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
-    const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, ab);
-  }
-};
 
 // Stationary-row fragments: lane holds row `row`, d = 16s + 8g .. +7 for every step s.
 template <int D>

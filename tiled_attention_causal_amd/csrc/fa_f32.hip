@@ -1,50 +1,117 @@
-// float32 attention forward and backward on the vector ALUs (no rounding below fp32
-// anywhere). This is the exact-arithmetic path for fp32 inputs; the bf16 path in fa_bf16.hip
-// is the one built for throughput.
+// float32 attention forward and backward on the fp32 matrix cores (v_mfma_f32_32x32x2_f32:
+// fp32 operands, fp32 accumulation; nothing is rounded below fp32).
 //
 // Method: "Systems and Parallelism" (CS336 field map, A2), section 1.2-1.3, problems
 // flash_forward (online softmax over key tiles, L = m + log l) and flash_backward
 // (P = exp(S - L), D = rowsum(dO o O), dS = P o (dP - D), scale in dQ and dK), with the
 // two-pass backward split of section 1.3.3.
 //
-// Each row (a query, or a key in the dK/dV pass) is owned by TPR = d/16 consecutive lanes,
-// each holding 16 of its d columns; dot products over d finish with group_sum<TPR>. The
-// moving rows are staged 32 at a time in LDS.
+// The 32x32x2 instruction: lane l gives A[l%32][l/32] and B[l/32][l%32], and register r of
+// lane l receives C[8(r/4) + 4(l/32) + r%4][l%32]. Every product here runs its reduction in
+// steps sigma of two, lane half g supplying index perm(sigma, g) = 8(sigma/4) + 4g + sigma%4:
+// over d that lets a lane read its operands as 16-byte groups (d = 8t + 4g .. +3 for steps
+// 4t .. 4t+3), and over 32 keys or queries it is exactly the row order of a C fragment, so a
+// product's output registers feed the next product as its B operand with no data movement:
+//   forward:  S^T = K Q^T (keys in registers, queries on lanes), P^T from S^T, O^T += V^T P^T;
+//   dK, dV:   S = Q K^T and dP = dO V^T (queries in registers, keys on lanes),
+//             dV^T += dO^T P and dK^T += Q^T dS;
+//   dQ:       S^T = K Q^T and dP^T = V dO^T, dQ^T += K^T dS^T.
+// The stationary operand of each kernel (Q; K and V; Q and dO) sits in registers; the moving
+// rows stream through double-buffered LDS tiles of 32 rows (direct loads, swizzled chunks).
+// Rows past a head's end load as zeros and are masked or never stored.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kT = 32;  // moving rows per LDS tile
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
 
+// 32 fp32 rows of D columns in LDS: the bf16-unit Tile with twice the columns (same bytes).
 template <int D>
-struct F32Cfg {
-  static constexpr int TPR = D / 16;    // lanes per row
-  static constexpr int RPB = 256 / TPR;  // rows per workgroup
+struct FTile {
+  using T = Tile<32, 2 * D>;
+  static constexpr int NCH = D / 4;  // 16-byte chunks per row
+  static constexpr int ELEMS = T::ELEMS;
+  __device__ __forceinline__ static void load(rsrc_t src, int row0, bf16* t, int w, int lane) {
+    T::template load<4>(src, row0, t, w, lane);
+  }
+  // Columns 4c .. 4c+3 of row r.
+  __device__ __forceinline__ static f32x4 quad(const bf16* t, int r, int c) {
+    return *reinterpret_cast<const f32x4*>(t + swz<NCH>(r, c));
+  }
+  // Column col of row r.
+  __device__ __forceinline__ static float at(const bf16* t, int r, int col) {
+    return *reinterpret_cast<const float*>(t + swz<NCH>(r, col >> 2) + 2 * (col & 3));
+  }
 };
 
-__device__ __forceinline__ void ld16(float (&x)[16], const float* p) {
+// Row `row` of a head as this lane's operand groups: x[t] = columns 8t + 4g .. +3.
+template <int D>
+__device__ __forceinline__ void load_row_quads(f32x4 (&x)[D / 8], rsrc_t head, int row, int g) {
 #pragma unroll
-  for (int i = 0; i < 16; i += 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
-    x[i] = v[0];
-    x[i + 1] = v[1];
-    x[i + 2] = v[2];
-    x[i + 3] = v[3];
+  for (int t = 0; t < D / 8; ++t)
+    x[t] = __builtin_bit_cast(f32x4, buf_load16(head, (uint32_t)((row * D + 8 * t + 4 * g) * 4)));
+}
+
+// C^T += (rows from LDS)·(registers): c += sum over d of A[i][d] b[j][d], with A row i = lane
+// l32 of the LDS tile and b this lane's register quads (perm order over d).
+template <int D>
+__device__ __forceinline__ f32x16 rows_times_regs(const bf16* tile, int l32, int g,
+                                                  const f32x4 (&b)[D / 8], f32x16 c) {
+#pragma unroll
+  for (int t = 0; t < D / 8; ++t) {
+    const f32x4 a = FTile<D>::quad(tile, l32, 2 * t + g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = mfma_f32(a[e], b[t][e], c);
   }
+  return c;
+}
+
+// acc[db] += (LDS tile rows transposed)·(32-row C fragment p): acc[db][d][j] += sum over the
+// tile's 32 rows u of tile[u][32 db + d] p[u][j], with p this lane's registers (row perm order).
+template <int D>
+__device__ __forceinline__ void cols_times_frag(const bf16* tile, int l32, int g,
+                                                const f32x16& p, f32x16 (&acc)[(D + 31) / 32]) {
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db) {
+    int col = 32 * db + l32;
+    if constexpr (D < 32) col &= D - 1;  // d = 16: the block's unused half re-reads valid columns
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int u = 8 * (s >> 2) + 4 * g + (s & 3);
+      acc[db] = mfma_f32(FTile<D>::at(tile, u, col), p[s], acc[db]);
+    }
+  }
+}
+
+// Store a transposed accumulator as rows: lane owns row `row`, register r of block db holds
+// column 32db + 8(r/4) + 4g + r%4.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float* out_row, const f32x16 (&acc)[(D + 31) / 32],
+                                               float mul, int g) {
+#pragma unroll
+  for (int db = 0; db < (D + 31) / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * db + 8 * j + 4 * g;
+      if (d0 < D)
+        *reinterpret_cast<f32x4*>(out_row + d0) =
+            f32x4{acc[db][4 * j] * mul, acc[db][4 * j + 1] * mul, acc[db][4 * j + 2] * mul,
+                  acc[db][4 * j + 3] * mul};
+    }
 }
 
 template <int D>
-__device__ __forceinline__ void stage_rows(float* tile, const float* head, int row0, int nrows) {
-  for (int i = threadIdx.x; i < kT * D / 4; i += 256) {
-    const int row = i / (D / 4), c4 = i % (D / 4);
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (row0 + row < nrows) v = *reinterpret_cast<const f32x4*>(head + (size_t)(row0 + row) * D + 4 * c4);
-    *reinterpret_cast<f32x4*>(tile + row * D + 4 * c4) = v;
-  }
+__device__ __forceinline__ void negate_quads(f32x4 (&x)[D / 8]) {
+#pragma unroll
+  for (int t = 0; t < D / 8; ++t) x[t] = -x[t];
 }
 
+// Forward: 128 query rows per workgroup (32 per wave, one per lane; the lane halves split the
+// keys of each tile), key tiles of 32.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q,
                                                       const float* __restrict__ K,
@@ -52,230 +119,274 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
                                                       float* __restrict__ O,
                                                       float* __restrict__ Lout, int Nq, int Nk,
                                                       float scale) {
-  constexpr int TPR = F32Cfg<D>::TPR, RPB = F32Cfg<D>::RPB;
-  __shared__ __attribute__((aligned(16))) float sK[kT * D];
-  __shared__ __attribute__((aligned(16))) float sV[kT * D];
-  const int nrt = (Nq + RPB - 1) / RPB;
-  const int bh = blockIdx.x / nrt, rt = blockIdx.x % nrt;
-  const int r0 = rt * RPB;
-  const int row = r0 + threadIdx.x / TPR, part = threadIdx.x % TPR;
-  const float* Qh = Q + (size_t)bh * Nq * D;
-  const float* Kh = K + (size_t)bh * Nk * D;
-  const float* Vh = V + (size_t)bh * Nk * D;
+  constexpr int DB = (D + 31) / 32, NT = D / 8;
+  using FT = FTile<D>;
+  __shared__ __attribute__((aligned(1024))) bf16 sk[2][FT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sv[2][FT::ELEMS];
+  const int nqt = (Nq + 127) / 128;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nqt, it = CAUSAL ? nqt - 1 - lid % nqt : lid % nqt;  // longest first
+  const int q0 = it * 128;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int qw0 = q0 + 32 * w, qrow = qw0 + l32;
+  const rsrc_t Qr = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 4);
+  const rsrc_t Kr = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
+  const rsrc_t Vr = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
+  const float cs = fabsf(scale), c = exp2_coef(scale);
 
-  float q[16], acc[16];
-  if (row < Nq) ld16(q, Qh + (size_t)row * D + 16 * part);
-  else
+  // With a negative scale the scores are taken of -Q, so that every score below is
+  // multiplied by |scale| and the row maxima stay maxima.
+  f32x4 qf[NT];
+  load_row_quads<D>(qf, Qr, qrow, g);
+  if (scale < 0.f) negate_quads<D>(qf);
+  f32x16 o[DB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  float m = -INFINITY, l = 0.f;  // row max of the raw scores, this lane half's sum of p
 
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(r0 + RPB, Nq));  // keys <= last row of this workgroup
-  for (int k0 = 0; k0 < kend; k0 += kT) {
-    __syncthreads();
-    stage_rows<D>(sK, Kh, k0, Nk);
-    stage_rows<D>(sV, Vh, k0, Nk);
-    __syncthreads();
-    float s[kT];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kT; ++j) {
-      float kk[16];
-      ld16(kk, sK + j * D + 16 * part);
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dot = fmaf(q[i], kk[i], dot);
-      dot = group_sum<TPR>(dot) * scale;
-      const int key = k0 + j;
-      if (key >= Nk || (CAUSAL && key > row)) dot = -INFINITY;
-      s[j] = dot;
-      mx = fmaxf(mx, dot);
-    }
-    const float mnew = fmaxf(m, mx);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = expf(m - mref);
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] *= alpha;
-#pragma unroll
-    for (int j = 0; j < kT; ++j) {
-      const float p = expf(s[j] - mref);
-      rs += p;
-      float vv[16];
-      ld16(vv, sV + j * D + 16 * part);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p, vv[i], acc[i]);
-    }
-    l = l * alpha + rs;
-    m = mnew;
+  const int kend = CAUSAL ? min(Nk, min(q0 + 128, Nq)) : Nk;  // keys the last row can see
+  const int nkt = (kend + 31) / 32;
+  if (nkt > 0) {
+    FT::load(Kr, 0, sk[0], w, lane);
+    FT::load(Vr, 0, sv[0], w, lane);
   }
-  if (row < Nq) {
-    const float inv = 1.f / l;
-    float* Op = O + ((size_t)bh * Nq + row) * D + 16 * part;
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bf16* ck = sk[kt & 1];
+    const bf16* cv = sv[kt & 1];
+    const int k0 = kt * 32;
+    if (kt + 1 < nkt) {
+      FT::load(Kr, k0 + 32, sk[(kt + 1) & 1], w, lane);
+      FT::load(Vr, k0 + 32, sv[(kt + 1) & 1], w, lane);
+    }
+    if (!CAUSAL || k0 <= qw0 + 31) {
+      // S^T: register r holds key k0 + 8(r/4) + 4g + r%4 against this lane's query.
+      f32x16 s[1] = {rows_times_regs<D>(ck, l32, g, qf, zero16())};
+      if ((CAUSAL && k0 + 31 > qw0) || k0 + 32 > Nk)
+        mask_scores<1>(s, 0, min(CAUSAL ? qrow - k0 - 4 * g : 1 << 30, Nk - 1 - k0 - 4 * g));
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      *reinterpret_cast<f32x4*>(Op + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv,
-                                                acc[i + 3] * inv};
-    if (part == 0) Lout[(size_t)bh * Nq + row] = m + logf(l);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      const float mnew = fmaxf(m, halves_max(mx));
+      const float mref = mnew == -INFINITY ? 0.f : mnew;  // no visible key yet: all p = 0
+      const float alpha = fast_exp2((m - mref) * c);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[0][r] = fast_exp2((s[0][r] - mref) * c);
+        ps += s[0][r];
+      }
+      l = l * alpha + ps;
+      m = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      cols_times_frag<D>(cv, l32, g, s[0], o);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  const float lt = halves_sum(l);
+  if (qrow < Nq) {
+    store_rows_f32<D>(O + ((size_t)bh * Nq + qrow) * D, o, 1.f / lt, g);
+    if (g == 0) Lout[(size_t)bh * Nq + qrow] = m * cs + logf(lt);
   }
 }
 
-// dK, dV: workgroup owns RPB keys and walks the query rows that can see them.
+// Backward. Per head the workgroups run the dK/dV key tiles (128 keys each, longest first)
+// and then the dQ query tiles (128 queries each, longest first).
+template <int D>
+struct F32Bwd {
+  static constexpr int DB = (D + 31) / 32, NT = D / 8;
+  static constexpr int TE = FTile<D>::ELEMS;
+  // dK/dV: Q, dO and O tiles per buffer; dQ: K and V tiles per buffer.
+  static constexpr int SMEM = 2 * 3 * TE;
+};
+
+// dK, dV for keys k0 .. k0+127. Per 32-query step: D_q = dO_q . O_q from the staged O and dO
+// (each wave for itself, through its own 32 words of LDS), L for the step's queries from
+// global memory (16 per lane), then the four products.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void dkdv_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ O, const float* __restrict__ L, const float* __restrict__ dO,
-    float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk, float scale) {
-  constexpr int TPR = F32Cfg<D>::TPR, RPB = F32Cfg<D>::RPB;
-  __shared__ __attribute__((aligned(16))) float sQ[kT * D];
-  __shared__ __attribute__((aligned(16))) float sdO[kT * D];
-  __shared__ float sL[kT], sD[kT];
-  const int nrt = (Nk + RPB - 1) / RPB;
-  const int bh = blockIdx.x / nrt, rt = blockIdx.x % nrt;
-  const int r0 = rt * RPB;
-  const int key = r0 + threadIdx.x / TPR, part = threadIdx.x % TPR;
-  const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
+__device__ __forceinline__ void dkdv_f32(bf16* smem, float* sdelta, rsrc_t Qr, rsrc_t Kr,
+                                         rsrc_t Vr, rsrc_t Or, rsrc_t Lr, rsrc_t dOr,
+                                         float* dKh, float* dVh, int k0, int Nq, int Nk,
+                                         float scale) {
+  using B = F32Bwd<D>;
+  using FT = FTile<D>;
+  constexpr int DB = B::DB, NT = B::NT, TE = B::TE;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int kw0 = k0 + 32 * w, krow = kw0 + l32;
+  const float c = exp2_coef(scale);
 
-  float k[16], v[16], dk[16], dv[16];
-  if (key < Nk) {
-    ld16(k, K + ok + (size_t)key * D + 16 * part);
-    ld16(v, V + ok + (size_t)key * D + 16 * part);
-  } else {
+  f32x4 kf[NT], vf[NT];
+  load_row_quads<D>(kf, Kr, krow, g);
+  load_row_quads<D>(vf, Vr, krow, g);
+  if (scale < 0.f) negate_quads<D>(kf);  // scores of -K: |scale| applies, as in the forward
+  f32x16 dk[DB], dv[DB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) k[i] = v[i] = 0.f;
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dk[i] = dv[i] = 0.f;
+  float* wdelta = sdelta + 32 * w;
 
-  const int qstart = CAUSAL ? (r0 / kT) * kT : 0;
-  for (int m0 = qstart; m0 < Nq; m0 += kT) {
-    __syncthreads();
-    stage_rows<D>(sQ, Q + oq, m0, Nq);
-    stage_rows<D>(sdO, dO + oq, m0, Nq);
-    if (threadIdx.x < kT) {
-      const int qi = m0 + threadIdx.x;
-      float dsum = 0.f, lv = 0.f;
-      if (qi < Nq) {
-        const float* op = O + oq + (size_t)qi * D;
-        const float* gp = dO + oq + (size_t)qi * D;
-        for (int i = 0; i < D; ++i) dsum = fmaf(gp[i], op[i], dsum);
-        lv = L[(size_t)bh * Nq + qi];
-      }
-      sL[threadIdx.x] = lv;
-      sD[threadIdx.x] = dsum;
-    }
-    __syncthreads();
-    for (int j = 0; j < kT; ++j) {
-      const int qi = m0 + j;
-      float qq[16], gg[16];
-      ld16(qq, sQ + j * D + 16 * part);
-      ld16(gg, sdO + j * D + 16 * part);
-      float sdot = 0.f, pdot = 0.f;
+  const int nmt = (Nq + 31) / 32;
+  const int mt0 = CAUSAL ? min(k0 / 32, nmt) : 0;
+  auto fetch = [&](int mt, int b) {
+    FT::load(Qr, mt * 32, smem + (3 * b + 0) * TE, w, lane);
+    FT::load(dOr, mt * 32, smem + (3 * b + 1) * TE, w, lane);
+    FT::load(Or, mt * 32, smem + (3 * b + 2) * TE, w, lane);
+  };
+  if (mt0 < nmt) fetch(mt0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int mt = mt0; mt < nmt; ++mt) {
+    const int b = (mt - mt0) & 1;
+    const bf16* cq = smem + (3 * b + 0) * TE;
+    const bf16* cdo = smem + (3 * b + 1) * TE;
+    const bf16* co = smem + (3 * b + 2) * TE;
+    const int m0 = mt * 32;
+    if (mt + 1 < nmt) fetch(mt + 1, b ^ 1);
+    if (!CAUSAL || m0 + 31 >= kw0) {
+      // D for query m0 + l32 (lane halves take alternate column quads), to this wave's LDS.
+      float dd = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sdot = fmaf(qq[i], k[i], sdot);
-        pdot = fmaf(gg[i], v[i], pdot);
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 x = FT::quad(cdo, l32, 2 * t + g), y = FT::quad(co, l32, 2 * t + g);
+        dd += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
       }
-      sdot = group_sum<TPR>(sdot);
-      pdot = group_sum<TPR>(pdot);
-      const bool vis = qi < Nq && (!CAUSAL || key <= qi);
-      const float p = vis ? expf(sdot * scale - sL[j]) : 0.f;
-      const float ds = p * (pdot - sD[j]);
+      dd = halves_sum(dd);
+      if (g == 0) wdelta[l32] = dd;
+      // L and D of this lane's 16 queries m0 + 8j + 4g + e (register 4j + e); L one word
+      // at a time, so that a ragged end reads zeros past Nq only.
+      f32x4 lq[4], dq[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dv[i] = fmaf(p, gg[i], dv[i]);
-        dk[i] = fmaf(ds, qq[i], dk[i]);
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lq[j][e] = buf_load_f32(Lr, (uint32_t)((m0 + 8 * j + 4 * g + e) * 4));
+        dq[j] = *reinterpret_cast<const f32x4*>(wdelta + 8 * j + 4 * g);
       }
+      // S = Q K^T and dP = dO V^T: register r holds query m0 + 8(r/4) + 4g + r%4, lane = key.
+      f32x16 s[1] = {rows_times_regs<D>(cq, l32, g, kf, zero16())};
+      f32x16 dp = rows_times_regs<D>(cdo, l32, g, vf, zero16());
+      if ((CAUSAL && m0 < kw0 + 31) || m0 + 32 > Nq)
+        mask_scores<1>(s, CAUSAL ? krow - m0 - 4 * g : -(1 << 30), Nq - 1 - m0 - 4 * g);
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[0][r] * c - lq[r >> 2][r & 3] * kLog2e);
+        s[0][r] = p;
+        ds[r] = p * (dp[r] - dq[r >> 2][r & 3]);
+      }
+      cols_times_frag<D>(cdo, l32, g, s[0], dv);  // dV^T += dO^T P
+      cols_times_frag<D>(cq, l32, g, ds, dk);     // dK^T += Q^T dS
     }
+    wait_vmem();
+    __syncthreads();
   }
-  if (key < Nk) {
-    float* kp = dK + ok + (size_t)key * D + 16 * part;
-    float* vp = dV + ok + (size_t)key * D + 16 * part;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      *reinterpret_cast<f32x4*>(kp + i) =
-          f32x4{dk[i] * scale, dk[i + 1] * scale, dk[i + 2] * scale, dk[i + 3] * scale};
-      *reinterpret_cast<f32x4*>(vp + i) = f32x4{dv[i], dv[i + 1], dv[i + 2], dv[i + 3]};
-    }
+
+  if (krow < Nk) {
+    store_rows_f32<D>(dKh + (size_t)krow * D, dk, scale, g);
+    store_rows_f32<D>(dVh + (size_t)krow * D, dv, 1.f, g);
   }
 }
 
-// dQ: workgroup owns RPB queries and walks the keys they can see.
+// dQ for queries q0 .. q0+127: Q, dO, L and D of the lane's query stay in registers.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void dq_f32_kernel(
+__device__ __forceinline__ void dq_f32(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
+                                       rsrc_t Lr, rsrc_t dOr, float* dQh, int q0, int Nq,
+                                       int Nk, float scale) {
+  using B = F32Bwd<D>;
+  using FT = FTile<D>;
+  constexpr int DB = B::DB, NT = B::NT, TE = B::TE;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int qw0 = q0 + 32 * w, qrow = qw0 + l32;
+  const float c = exp2_coef(scale);
+
+  f32x4 qf[NT], dof[NT];
+  load_row_quads<D>(qf, Qr, qrow, g);
+  load_row_quads<D>(dof, dOr, qrow, g);
+  float dd = 0.f;
+  {
+    f32x4 of[NT];
+    load_row_quads<D>(of, Or, qrow, g);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      dd += dof[t][0] * of[t][0] + dof[t][1] * of[t][1] + dof[t][2] * of[t][2] +
+            dof[t][3] * of[t][3];
+  }
+  dd = halves_sum(dd);
+  const float l2 = buf_load_f32(Lr, (uint32_t)(qrow * 4)) * kLog2e;
+  if (scale < 0.f) negate_quads<D>(qf);
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = zero16();
+
+  int nkt = (Nk + 31) / 32;
+  if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / 32 + 1);
+  if (nkt > 0) {
+    FT::load(Kr, 0, smem, w, lane);
+    FT::load(Vr, 0, smem + TE, w, lane);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int b = kt & 1;
+    const bf16* ck = smem + (2 * b + 0) * TE;
+    const bf16* cv = smem + (2 * b + 1) * TE;
+    const int k0 = kt * 32;
+    if (kt + 1 < nkt) {
+      FT::load(Kr, k0 + 32, smem + (2 * (b ^ 1) + 0) * TE, w, lane);
+      FT::load(Vr, k0 + 32, smem + (2 * (b ^ 1) + 1) * TE, w, lane);
+    }
+    if (!CAUSAL || k0 <= qw0 + 31) {
+      // S^T and dP^T: register r holds key k0 + 8(r/4) + 4g + r%4, lane = query.
+      f32x16 s[1] = {rows_times_regs<D>(ck, l32, g, qf, zero16())};
+      f32x16 dp = rows_times_regs<D>(cv, l32, g, dof, zero16());
+      if ((CAUSAL && k0 + 31 > qw0) || k0 + 32 > Nk)
+        mask_scores<1>(s, 0, min(CAUSAL ? qrow - k0 - 4 * g : 1 << 30, Nk - 1 - k0 - 4 * g));
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(s[0][r] * c - l2) * (dp[r] - dd);
+      cols_times_frag<D>(ck, l32, g, ds, dqa);  // dQ^T += K^T dS^T
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (qrow < Nq) store_rows_f32<D>(dQh + (size_t)qrow * D, dqa, scale, g);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ O, const float* __restrict__ L, const float* __restrict__ dO,
-    float* __restrict__ dQ, int Nq, int Nk, float scale) {
-  constexpr int TPR = F32Cfg<D>::TPR, RPB = F32Cfg<D>::RPB;
-  __shared__ __attribute__((aligned(16))) float sK[kT * D];
-  __shared__ __attribute__((aligned(16))) float sV[kT * D];
-  const int nrt = (Nq + RPB - 1) / RPB;
-  const int bh = blockIdx.x / nrt, rt = blockIdx.x % nrt;
-  const int r0 = rt * RPB;
-  const int row = r0 + threadIdx.x / TPR, part = threadIdx.x % TPR;
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk,
+    float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16 smem[F32Bwd<D>::SMEM];
+  __shared__ __attribute__((aligned(16))) float sdelta[4 * 32];
+  const int nkv = (Nk + 127) / 128, nqw = (Nq + 127) / 128, per_head = nkv + nqw;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / per_head, idx = lid % per_head;
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
-
-  float q[16], g[16], dq[16];
-  float dsum = 0.f, lv = 0.f;
-  if (row < Nq) {
-    float o[16];
-    ld16(q, Q + oq + (size_t)row * D + 16 * part);
-    ld16(g, dO + oq + (size_t)row * D + 16 * part);
-    ld16(o, O + oq + (size_t)row * D + 16 * part);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dsum = fmaf(g[i], o[i], dsum);
-    lv = L[(size_t)bh * Nq + row];
+  const uint32_t bq = (uint32_t)Nq * D * 4, bk = (uint32_t)Nk * D * 4;
+  const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq), dOr = make_rsrc(dO + oq, bq);
+  const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
+  const rsrc_t Lr = make_rsrc(L + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  if (idx < nkv) {
+    dkdv_f32<D, CAUSAL>(smem, sdelta, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, idx * 128, Nq,
+                        Nk, scale);
   } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = g[i] = 0.f;
-  }
-  dsum = group_sum<TPR>(dsum);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dq[i] = 0.f;
-
-  int kend = Nk;
-  if (CAUSAL) kend = min(Nk, min(r0 + RPB, Nq));
-  for (int k0 = 0; k0 < kend; k0 += kT) {
-    __syncthreads();
-    stage_rows<D>(sK, K + ok, k0, Nk);
-    stage_rows<D>(sV, V + ok, k0, Nk);
-    __syncthreads();
-    for (int j = 0; j < kT; ++j) {
-      const int key = k0 + j;
-      float kk[16], vv[16];
-      ld16(kk, sK + j * D + 16 * part);
-      ld16(vv, sV + j * D + 16 * part);
-      float sdot = 0.f, pdot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sdot = fmaf(q[i], kk[i], sdot);
-        pdot = fmaf(g[i], vv[i], pdot);
-      }
-      sdot = group_sum<TPR>(sdot);
-      pdot = group_sum<TPR>(pdot);
-      const bool vis = row < Nq && key < Nk && (!CAUSAL || key <= row);
-      const float p = vis ? expf(sdot * scale - lv) : 0.f;
-      const float ds = p * (pdot - dsum);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dq[i] = fmaf(ds, kk[i], dq[i]);
-    }
-  }
-  if (row < Nq) {
-    float* qp = dQ + oq + (size_t)row * D + 16 * part;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      *reinterpret_cast<f32x4*>(qp + i) =
-          f32x4{dq[i] * scale, dq[i + 1] * scale, dq[i + 2] * scale, dq[i + 3] * scale};
+    const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
+    dq_f32<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_t(const Shape& s, const float* Q, const float* K, const float* V, float* O,
                  float* L, hipStream_t stream) {
-  const long long grid = (long long)((s.Nq + F32Cfg<D>::RPB - 1) / F32Cfg<D>::RPB) * s.BH;
+  const long long grid = (long long)((s.Nq + 127) / 128) * s.BH;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, Q,
                      K, V, O, L, s.Nq, s.Nk, s.scale);
   return hipGetLastError();
@@ -285,21 +396,11 @@ template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const float* Q, const float* K, const float* V, const float* O,
                  const float* L, const float* dO, float* dQ, float* dK, float* dV,
                  hipStream_t stream) {
-  constexpr int RPB = F32Cfg<D>::RPB;
-  const long long gkv = (long long)((s.Nk + RPB - 1) / RPB) * s.BH;
-  if (gkv > 0) {
-    hipLaunchKernelGGL((dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)gkv), dim3(256), 0, stream,
-                       Q, K, V, O, L, dO, dK, dV, s.Nq, s.Nk, s.scale);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const long long gq = (long long)((s.Nq + RPB - 1) / RPB) * s.BH;
-  if (gq > 0) {
-    hipLaunchKernelGGL((dq_f32_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream, Q,
-                       K, V, O, L, dO, dQ, s.Nq, s.Nk, s.scale);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, Q,
+                     K, V, O, L, dO, dQ, dK, dV, s.Nq, s.Nk, s.scale);
+  return hipGetLastError();
 }
 
 }  // namespace
