@@ -58,7 +58,7 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # bf16: L log2(e) and -D per query row; fp32: none; rejected sizes report 0.
+    # bf16: L log2(e) and -D per query row; fp32: none of those; rejected sizes report 0.
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 64) == 8 * 4096 * 8
     # Small square grids add room for fp32 partial sums: 64-row tiles x ways x 48 * d/32
     # floats x 128 lanes (B*H = 1, N = 8192, d = 64: 128 tiles, 4 ways).
@@ -74,7 +74,10 @@ def test_workspace_sizes(lib):
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 8192, 8192, 128) == 8 * 8192 * 8
     assert lib.fa_backward_workspace_bytes(1, 4, 25, 2048, 1024, 128) == 100 * 2048 * 8
     assert lib.fa_backward_workspace_bytes(1, 2, 3, 0, 64, 64) == 0
-    assert lib.fa_backward_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 0
+    # fp32: only the partial sums of small grids (8 heads of 4096 at d = 64: causal 2 ways).
+    assert lib.fa_backward_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 64 * 8 * 2 * 192 * 64 * 4
+    assert lib.fa_backward_workspace_bytes(0, 16, 8, 4096, 4096, 64) == 0   # fills the CUs
+    assert lib.fa_backward_workspace_bytes(0, 1, 1, 4000, 4000, 64) == 0    # not 128-aligned
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 4096, 4096, 48) == 0
     assert lib.fa_backward_workspace_bytes(1, -1, 1, 4096, 4096, 64) == 0
 
@@ -92,7 +95,9 @@ def test_forward_workspace_sizes(lib):
     assert ws(1, 1, 1, 8192, 8192, 128, 1) == 64 * 4 * 2 * 66 * 128 * 4
     assert ws(1, 1, 1, 8192, 8192, 16, 1) == 64 * 4 * 2 * 18 * 128 * 4  # split kernel, d = 16
     assert ws(1, 1, 1, 8192, 4096, 64, 1) == 0      # Nq != Nk
-    assert ws(0, 1, 1, 8192, 8192, 64, 1) == 0      # fp32
+    # fp32: 64 query tiles x 8 ways x (16 * ceil(d/32) + 2) floats x 256 lanes
+    assert ws(0, 1, 1, 8192, 8192, 64, 1) == 64 * 8 * 34 * 256 * 4
+    assert ws(0, 16, 8, 8192, 8192, 64, 1) == 0     # fp32 grid that fills the CUs
     assert ws(1, 1, 1, 256, 256, 64, 1) == 0        # runs would be too short
     assert ws(1, -1, 1, 8192, 8192, 64, 1) == 0     # rejected arguments
 

@@ -320,6 +320,31 @@ def test_backward_split_over_workgroups_matches_oracle(gpu, case):
     compare(got, full_oracle(inp, causal, scale, heads), "bf16", heads)
 
 
+# fp32 small grids: the forward spreads each query tile's keys, the backward each workgroup's
+# steps, over several workgroups whose partial results a second launch merges or adds.
+SPLIT_F32 = [
+    (1, 1, 2048, 64, True),
+    (1, 2, 1024, 128, True),
+    (1, 1, 1024, 16, False),
+    (2, 1, 2048, 32, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_F32, ids=lambda c: "B{}H{}N{}d{}{}".format(
+    *c[:4], "causal" if c[4] else "full"))
+def test_fp32_split_over_workgroups_matches_oracle(gpu, case):
+    from tiled_attention_causal_amd import backward_workspace_bytes, forward_workspace_bytes
+    B, H, N, d, causal = case
+    note(f"fp32 split case {case}")
+    inp = make_inputs(B, H, N, N, d, "f32", index=9500 + N + d + H + causal)
+    assert forward_workspace_bytes(inp["q"], inp["k"], causal) > 0
+    assert backward_workspace_bytes(inp["q"], inp["k"]) > 0
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, causal, scale, gpu)
+    heads = [(0, 0), (B - 1, H - 1)]
+    compare(got, full_oracle(inp, causal, scale, heads), "f32", heads)
+
+
 @pytest.mark.parametrize("d,causal", [(64, True), (128, True), (64, False)])
 def test_backward_minimum_workspace_matches_split(gpu, d, causal):
     """A workspace of only the per-row terms: the same grid runs unsplit, which changes only

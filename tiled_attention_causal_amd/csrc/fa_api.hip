@@ -72,7 +72,9 @@ size_t fa_backward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t
   fa::Shape s;
   if (check_common(dtype, B, H, Nq, Nk, d, 1.f, 0, &s) != FA_SUCCESS) return 0;
   const size_t rows = backward_rows_bytes(dtype, s);
-  // Room for the partial sums of small causal grids (used only when the call is causal).
+  // Room for the partial sums of small grids (the larger of the causal and the non-causal
+  // call's), after the per-row terms (bf16 only).
+  if (dtype == FA_DTYPE_F32) return fa::bwd_split_workspace_bytes_f32(s);
   return rows > 0 ? rows + fa::bwd_split_workspace_bytes_bf16(s) : 0;
 }
 
@@ -80,7 +82,8 @@ size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t 
                                   int64_t d, int is_causal) {
   fa::Shape s;
   if (check_common(dtype, B, H, Nq, Nk, d, 1.f, is_causal, &s) != FA_SUCCESS) return 0;
-  return dtype == FA_DTYPE_BF16 ? fa::fwd_workspace_bytes_bf16(s) : 0;
+  return dtype == FA_DTYPE_BF16 ? fa::fwd_workspace_bytes_bf16(s)
+                                : fa::fwd_workspace_bytes_f32(s);
 }
 
 fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
@@ -104,7 +107,8 @@ fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
                             hs);
   else
     e = fa::launch_fwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
-                           static_cast<const float*>(V), static_cast<float*>(O), L, hs);
+                           static_cast<const float*>(V), static_cast<float*>(O), L,
+                           static_cast<float*>(workspace), workspace_bytes, hs);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
 }
 
@@ -170,7 +174,8 @@ fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
     e = fa::launch_bwd_f32(s, static_cast<const float*>(Q), static_cast<const float*>(K),
                            static_cast<const float*>(V), static_cast<const float*>(O), L,
                            static_cast<const float*>(dO), static_cast<float*>(dQ),
-                           static_cast<float*>(dK), static_cast<float*>(dV), hs);
+                           static_cast<float*>(dK), static_cast<float*>(dV),
+                           static_cast<float*>(workspace), workspace_bytes, hs);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
 }
 

@@ -29,8 +29,6 @@
 namespace fa {
 namespace {
 
-constexpr int kNumCUs = 256;  // MI355X
-
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   u32x4 u = __builtin_bit_cast(u32x4, x);
   u ^= 0x80008000u;

@@ -19,11 +19,15 @@
 // The stationary operand of each kernel (Q; K and V; Q and dO) sits in registers; the moving
 // rows stream through double-buffered LDS tiles of 32 rows (direct loads, swizzled chunks).
 // Rows past a head's end load as zeros and are masked or never stored.
+#include <algorithm>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
+
+constexpr int kMinSteps = 8, kMaxShares = 8;  // split grids: see f32_ways
 
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -110,22 +114,56 @@ __device__ __forceinline__ void negate_quads(f32x4 (&x)[D / 8]) {
   for (int t = 0; t < D / 8; ++t) x[t] = -x[t];
 }
 
+// Runs step(n, cur) for n = first .. last-1 over tiles that fetch(n, dst) loads straight into
+// LDS, one tile ahead, through two buffers. The loop is unrolled by two inside one function
+// whose buffers are restrict parameters, so every access names its buffer statically: the
+// compiler can tell that a step's LDS reads of `cur` do not alias the loads in flight into
+// the other buffer and does not wait for those loads before reading.
+template <class Fetch, class Step>
+__device__ __forceinline__ void stream2(int first, int last, bf16* __restrict__ b0,
+                                        bf16* __restrict__ b1, Fetch&& fetch, Step&& step) {
+  if (first < last) fetch(first, b0);
+  wait_vmem();
+  __syncthreads();
+  for (int n = first; n < last; n += 2) {
+    if (n + 1 < last) fetch(n + 1, b1);
+    step(n, b0);
+    wait_vmem();
+    __syncthreads();
+    if (n + 1 < last) {
+      if (n + 2 < last) fetch(n + 2, b0);
+      step(n + 1, b1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+}
+
 // Forward: 128 query rows per workgroup (32 per wave, one per lane; the lane halves split the
 // keys of each tile), key tiles of 32.
+//
+// Small grids spread each query tile's key tiles over ns workgroups (consecutive blocks, in
+// dispatch order, so that every XCD gets an even mix of long and short shares): share sw runs
+// the sw-th of ns equal slices and writes its partial (unnormalised O, m, l) per lane to
+// part + ((bh nqt + it) ns + sw) XS 256, component k of thread t at k 256 + t, for
+// fwd_f32_combine_kernel to merge.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q,
                                                       const float* __restrict__ K,
                                                       const float* __restrict__ V,
                                                       float* __restrict__ O,
                                                       float* __restrict__ Lout, int Nq, int Nk,
-                                                      float scale) {
-  constexpr int DB = (D + 31) / 32, NT = D / 8;
+                                                      float scale, int ns,
+                                                      float* __restrict__ part) {
+  constexpr int DB = (D + 31) / 32, NT = D / 8, XS = 16 * DB + 2;
   using FT = FTile<D>;
-  __shared__ __attribute__((aligned(1024))) bf16 sk[2][FT::ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 sv[2][FT::ELEMS];
+  constexpr int TE = FT::ELEMS;
+  __shared__ __attribute__((aligned(1024))) bf16 buf0[2 * TE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) bf16 buf1[2 * TE];
   const int nqt = (Nq + 127) / 128;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / nqt, it = CAUSAL ? nqt - 1 - lid % nqt : lid % nqt;  // longest first
+  const int lid = ns > 1 ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int sw = lid % ns, pid = lid / ns;
+  const int bh = pid / nqt, it = CAUSAL ? nqt - 1 - pid % nqt : pid % nqt;  // longest first
   const int q0 = it * 128;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int qw0 = q0 + 32 * w, qrow = qw0 + l32;
@@ -146,20 +184,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
   const int kend = CAUSAL ? min(Nk, min(q0 + 128, Nq)) : Nk;  // keys the last row can see
   const int nkt = (kend + 31) / 32;
-  if (nkt > 0) {
-    FT::load(Kr, 0, sk[0], w, lane);
-    FT::load(Vr, 0, sv[0], w, lane);
-  }
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bf16* ck = sk[kt & 1];
-    const bf16* cv = sv[kt & 1];
+  const int lo = sw * nkt / ns, hi = (sw + 1) * nkt / ns;
+  auto fetch = [&](int kt, bf16* dst) {
+    FT::load(Kr, kt * 32, dst, w, lane);
+    FT::load(Vr, kt * 32, dst + TE, w, lane);
+  };
+  auto step = [&](int kt, const bf16* cur) {
+    const bf16* ck = cur;
+    const bf16* cv = cur + TE;
     const int k0 = kt * 32;
-    if (kt + 1 < nkt) {
-      FT::load(Kr, k0 + 32, sk[(kt + 1) & 1], w, lane);
-      FT::load(Vr, k0 + 32, sv[(kt + 1) & 1], w, lane);
-    }
     if (!CAUSAL || k0 <= qw0 + 31) {
       // S^T: register r holds key k0 + 8(r/4) + 4g + r%4 against this lane's query.
       f32x16 s[1] = {rows_times_regs<D>(ck, l32, g, qf, zero16())};
@@ -183,14 +216,79 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       cols_times_frag<D>(cv, l32, g, s[0], o);
     }
-    wait_vmem();
-    __syncthreads();
-  }
+  };
+  stream2(lo, hi, buf0, buf1, fetch, step);
 
+  if (ns > 1) {
+    float* x = part + ((size_t)(bh * nqt + it) * ns + sw) * XS * 256 + tid;
+    asm volatile("" : "+v"(x));  // address formed here, not held through the loop
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[(16 * db + r) * 256] = o[db][r];
+    x[16 * DB * 256] = m;
+    x[(16 * DB + 1) * 256] = l;
+    return;
+  }
   const float lt = halves_sum(l);
   if (qrow < Nq) {
     store_rows_f32<D>(O + ((size_t)bh * Nq + qrow) * D, o, 1.f / lt, g);
     if (g == 0) Lout[(size_t)bh * Nq + qrow] = m * cs + logf(lt);
+  }
+}
+
+// Merges the ns partial records fwd_f32_kernel wrote for each 128-row query tile, with the
+// rescale the online softmax applies between key tiles, and stores O and L. Thread t takes
+// record lane t % 256 (the kernel's lane and wave, so the two lane halves of a row sum their
+// l as in the kernel) and 32-column block t / 256; all of its loads are independent. A share
+// with no visible key for a row has m = -inf and l = O = 0: weight 0.
+template <int D>
+__global__ __launch_bounds__(256 * ((D + 31) / 32)) void fwd_f32_combine_kernel(
+    const float* __restrict__ part, float* __restrict__ O, float* __restrict__ Lout, int Nq,
+    float scale, int ns) {
+  constexpr int DB = (D + 31) / 32, XS = 16 * DB + 2, MAXW = kMaxShares;
+  const int nqt = (Nq + 127) / 128;
+  const int bh = blockIdx.x / nqt, it = blockIdx.x % nqt;
+  const int slot = threadIdx.x & 255, db = threadIdx.x >> 8;
+  const int lane = slot & 63, w = slot >> 6, g = lane >> 5, l32 = lane & 31;
+  const float cs = fabsf(scale), c = exp2_coef(scale);
+  const float* x0 = part + (size_t)blockIdx.x * ns * XS * 256 + slot;
+  // Loads are unconditional (shares past ns re-read the last one and get weight 0), so the
+  // compiler can issue them all before the first use.
+  float mw[MAXW], lw[MAXW];
+#pragma unroll
+  for (int sh = 0; sh < MAXW; ++sh) {
+    const float* x = x0 + (size_t)min(sh, ns - 1) * XS * 256;
+    mw[sh] = x[16 * DB * 256];
+    lw[sh] = x[(16 * DB + 1) * 256];
+  }
+  float mm = mw[0];
+#pragma unroll
+  for (int sh = 1; sh < MAXW; ++sh) mm = fmaxf(mm, mw[sh]);
+  const float mref = mm == -INFINITY ? 0.f : mm;
+  f32x16 o = zero16();
+  float l = 0.f;
+#pragma unroll
+  for (int sh = 0; sh < MAXW; ++sh) {
+    const float f = sh < ns ? fast_exp2((mw[sh] - mref) * c) : 0.f;
+    const float* x = x0 + (size_t)min(sh, ns - 1) * XS * 256 + 16 * db * 256;
+    l += f * lw[sh];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] += f * x[r * 256];
+  }
+  const float lt = halves_sum(l);
+  const int qrow = it * 128 + 32 * w + l32;
+  if (qrow < Nq) {
+    float* orow = O + ((size_t)bh * Nq + qrow) * D;
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * db + 8 * j + 4 * g;
+      if (d0 < D)
+        *reinterpret_cast<f32x4*>(orow + d0) =
+            f32x4{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
+    }
+    if (g == 0 && db == 0) Lout[(size_t)bh * Nq + qrow] = mm * cs + logf(lt);
   }
 }
 
@@ -211,7 +309,7 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_f32(bf16* smem, float* sdelta, rsrc_t Qr, rsrc_t Kr,
                                          rsrc_t Vr, rsrc_t Or, rsrc_t Lr, rsrc_t dOr,
                                          float* dKh, float* dVh, int k0, int Nq, int Nk,
-                                         float scale) {
+                                         float scale, int sw, int ns, float* part) {
   using B = F32Bwd<D>;
   using FT = FTile<D>;
   constexpr int DB = B::DB, NT = B::NT, TE = B::TE;
@@ -233,21 +331,17 @@ __device__ __forceinline__ void dkdv_f32(bf16* smem, float* sdelta, rsrc_t Qr, r
 
   const int nmt = (Nq + 31) / 32;
   const int mt0 = CAUSAL ? min(k0 / 32, nmt) : 0;
-  auto fetch = [&](int mt, int b) {
-    FT::load(Qr, mt * 32, smem + (3 * b + 0) * TE, w, lane);
-    FT::load(dOr, mt * 32, smem + (3 * b + 1) * TE, w, lane);
-    FT::load(Or, mt * 32, smem + (3 * b + 2) * TE, w, lane);
+  const int lo = mt0 + sw * (nmt - mt0) / ns, hi = mt0 + (sw + 1) * (nmt - mt0) / ns;
+  auto fetch = [&](int mt, bf16* dst) {
+    FT::load(Qr, mt * 32, dst, w, lane);
+    FT::load(dOr, mt * 32, dst + TE, w, lane);
+    FT::load(Or, mt * 32, dst + 2 * TE, w, lane);
   };
-  if (mt0 < nmt) fetch(mt0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int mt = mt0; mt < nmt; ++mt) {
-    const int b = (mt - mt0) & 1;
-    const bf16* cq = smem + (3 * b + 0) * TE;
-    const bf16* cdo = smem + (3 * b + 1) * TE;
-    const bf16* co = smem + (3 * b + 2) * TE;
+  auto step = [&](int mt, const bf16* cur) {
+    const bf16* cq = cur;
+    const bf16* cdo = cur + TE;
+    const bf16* co = cur + 2 * TE;
     const int m0 = mt * 32;
-    if (mt + 1 < nmt) fetch(mt + 1, b ^ 1);
     if (!CAUSAL || m0 + 31 >= kw0) {
       // D for query m0 + l32 (lane halves take alternate column quads), to this wave's LDS.
       float dd = 0.f;
@@ -283,11 +377,15 @@ __device__ __forceinline__ void dkdv_f32(bf16* smem, float* sdelta, rsrc_t Qr, r
       cols_times_frag<D>(cdo, l32, g, s[0], dv);  // dV^T += dO^T P
       cols_times_frag<D>(cq, l32, g, ds, dk);     // dK^T += Q^T dS
     }
-    wait_vmem();
-    __syncthreads();
-  }
+  };
+  stream2(lo, hi, smem, smem + 3 * TE, fetch, step);
 
-  if (krow < Nk) {
+  if (ns > 1) {  // Nq = Nk, a multiple of 128: every row exists
+    float* x = part + (((size_t)(krow / 64) * ns + sw) * 2 * 64 + krow % 64) * D;
+    asm volatile("" : "+v"(x));
+    store_rows_f32<D>(x, dk, 1.f, g);
+    store_rows_f32<D>(x + 64 * D, dv, 1.f, g);
+  } else if (krow < Nk) {
     store_rows_f32<D>(dKh + (size_t)krow * D, dk, scale, g);
     store_rows_f32<D>(dVh + (size_t)krow * D, dv, 1.f, g);
   }
@@ -297,7 +395,7 @@ __device__ __forceinline__ void dkdv_f32(bf16* smem, float* sdelta, rsrc_t Qr, r
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_f32(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t Vr, rsrc_t Or,
                                        rsrc_t Lr, rsrc_t dOr, float* dQh, int q0, int Nq,
-                                       int Nk, float scale) {
+                                       int Nk, float scale, int sw, int ns, float* part) {
   using B = F32Bwd<D>;
   using FT = FTile<D>;
   constexpr int DB = B::DB, NT = B::NT, TE = B::TE;
@@ -326,21 +424,15 @@ __device__ __forceinline__ void dq_f32(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t 
 
   int nkt = (Nk + 31) / 32;
   if (CAUSAL) nkt = min(nkt, (min(q0 + 128, Nq) - 1) / 32 + 1);
-  if (nkt > 0) {
-    FT::load(Kr, 0, smem, w, lane);
-    FT::load(Vr, 0, smem + TE, w, lane);
-  }
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int b = kt & 1;
-    const bf16* ck = smem + (2 * b + 0) * TE;
-    const bf16* cv = smem + (2 * b + 1) * TE;
+  const int lo = sw * nkt / ns, hi = (sw + 1) * nkt / ns;
+  auto fetch = [&](int kt, bf16* dst) {
+    FT::load(Kr, kt * 32, dst, w, lane);
+    FT::load(Vr, kt * 32, dst + TE, w, lane);
+  };
+  auto step = [&](int kt, const bf16* cur) {
+    const bf16* ck = cur;
+    const bf16* cv = cur + TE;
     const int k0 = kt * 32;
-    if (kt + 1 < nkt) {
-      FT::load(Kr, k0 + 32, smem + (2 * (b ^ 1) + 0) * TE, w, lane);
-      FT::load(Vr, k0 + 32, smem + (2 * (b ^ 1) + 1) * TE, w, lane);
-    }
     if (!CAUSAL || k0 <= qw0 + 31) {
       // S^T and dP^T: register r holds key k0 + 8(r/4) + 4g + r%4, lane = query.
       f32x16 s[1] = {rows_times_regs<D>(ck, l32, g, qf, zero16())};
@@ -352,23 +444,35 @@ __device__ __forceinline__ void dq_f32(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t 
       for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(s[0][r] * c - l2) * (dp[r] - dd);
       cols_times_frag<D>(ck, l32, g, ds, dqa);  // dQ^T += K^T dS^T
     }
-    wait_vmem();
-    __syncthreads();
+  };
+  stream2(lo, hi, smem, smem + 3 * TE, fetch, step);
+  if (ns > 1) {
+    float* x = part + ((size_t)(qrow / 64) * ns + sw) * 64 * D + (size_t)(qrow % 64) * D;
+    asm volatile("" : "+v"(x));
+    store_rows_f32<D>(x, dqa, 1.f, g);
+  } else if (qrow < Nq) {
+    store_rows_f32<D>(dQh + (size_t)qrow * D, dqa, scale, g);
   }
-  if (qrow < Nq) store_rows_f32<D>(dQh + (size_t)qrow * D, dqa, scale, g);
 }
 
+// Small grids (Nq = Nk = N, N % 128 == 0) spread each workgroup's steps over ns workgroups,
+// in dispatch order, as in the forward; share sw writes unscaled fp32 partial sums per 64-row
+// tile t of head bh as [64][D] rows: dK^T and dV^T at kvpart + ((bh T + t) ns + sw) 2 * 64 D
+// (dV^T after dK^T), dQ^T at qpart + ((bh T + t) ns + sw) 64 D, T = N / 64, for
+// bwd_f32_combine_kernel to add up.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ O, const float* __restrict__ L, const float* __restrict__ dO,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Nq, int Nk,
-    float scale) {
+    float scale, int ns, float* __restrict__ kvpart, float* __restrict__ qpart) {
   __shared__ __attribute__((aligned(1024))) bf16 smem[F32Bwd<D>::SMEM];
   __shared__ __attribute__((aligned(16))) float sdelta[4 * 32];
   const int nkv = (Nk + 127) / 128, nqw = (Nq + 127) / 128, per_head = nkv + nqw;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / per_head, idx = lid % per_head;
+  const int lid = ns > 1 ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int sw = lid % ns, pid = lid / ns;
+  const int bh = pid / per_head, idx = pid % per_head;
+  const size_t head_part = (size_t)bh * (Nq / 64) * ns * 64 * D;  // one tensor's tiles per head
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
   const uint32_t bq = (uint32_t)Nq * D * 4, bk = (uint32_t)Nk * D * 4;
   const rsrc_t Qr = make_rsrc(Q + oq, bq), Or = make_rsrc(O + oq, bq), dOr = make_rsrc(dO + oq, bq);
@@ -376,41 +480,134 @@ __global__ __launch_bounds__(256) void bwd_f32_kernel(
   const rsrc_t Lr = make_rsrc(L + (size_t)bh * Nq, (uint32_t)Nq * 4);
   if (idx < nkv) {
     dkdv_f32<D, CAUSAL>(smem, sdelta, Qr, Kr, Vr, Or, Lr, dOr, dK + ok, dV + ok, idx * 128, Nq,
-                        Nk, scale);
+                        Nk, scale, sw, ns, ns > 1 ? kvpart + 2 * head_part : nullptr);
   } else {
     const int it = CAUSAL ? nqw - 1 - (idx - nkv) : idx - nkv;
-    dq_f32<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale);
+    dq_f32<D, CAUSAL>(smem, Qr, Kr, Vr, Or, Lr, dOr, dQ + oq, it * 128, Nq, Nk, scale, sw, ns,
+                      ns > 1 ? qpart + head_part : nullptr);
   }
+}
+
+// Adds the ns partial [64][D] tiles bwd_f32_kernel wrote for each 64-row tile, scales dK and
+// dQ, and stores dQ, dK and dV: one float4 of one tensor per thread, summed over the shares
+// with independent loads; a tile's three tensors take 3 * 64 * D / 1024 workgroups.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_f32_combine_kernel(
+    const float* __restrict__ kvpart, const float* __restrict__ qpart, float* __restrict__ dQ,
+    float* __restrict__ dK, float* __restrict__ dV, int N, float scale, int ns) {
+  constexpr int MAXW = 8, TILE = 64 * D, BLOCKS = 3 * TILE / 1024;
+  const int T = N / 64;
+  const int tb = blockIdx.x / BLOCKS, blk = blockIdx.x % BLOCKS;
+  const int tile = tb % T, bh = tb / T;
+  const size_t base = ((size_t)bh * T + tile) * ns;
+  const int e = blk * 1024 + 4 * threadIdx.x;
+  const int tensor = e / TILE, k = e % TILE;  // 0: dK, 1: dV, 2: dQ
+  const float* x = tensor < 2 ? kvpart + base * 2 * TILE + tensor * TILE + k
+                              : qpart + base * TILE + k;
+  const size_t stride = tensor < 2 ? 2 * TILE : TILE;
+  f32x4 v[MAXW];
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < ns) v[w] = *reinterpret_cast<const f32x4*>(x + w * stride);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w)
+    if (w < ns) acc += v[w];
+  float* out = tensor == 0 ? dK : (tensor == 1 ? dV : dQ);
+  *reinterpret_cast<f32x4*>(out + ((size_t)bh * N + 64 * tile) * D + k) =
+      acc * (tensor == 1 ? 1.f : scale);
+}
+
+// Workgroups per workgroup for small fp32 grids: doubling (up to 8) while every share keeps
+// at least kMinSteps steps of 32 rows and the grid stays within the CUs' room for the kernel's
+// workgroups (two per CU at d <= 64, one at d = 128), or twice that for causal grids, whose
+// shares differ in length: dispatched longest first, the short ones fill in behind the long.
+int f32_ways(long long wgs, int steps, const Shape& s) {
+  const long long room = (long long)kNumCUs * (s.d <= 64 ? 2 : 1) * (s.causal ? 2 : 1);
+  int ns = 1;
+  while (ns < kMaxShares && wgs * ns * 2 <= room && steps / (ns * 2) >= kMinSteps) ns *= 2;
+  return ns;
+}
+int fwd_f32_ways(const Shape& s) {
+  const int steps = ((s.causal ? std::min(s.Nq, s.Nk) : s.Nk) + 31) / 32;  // longest tile's
+  return f32_ways((long long)((s.Nq + 127) / 128) * s.BH, steps, s);
+}
+int bwd_f32_ways(const Shape& s) {
+  if (s.Nq != s.Nk || s.Nq % 128 != 0) return 1;  // partial sums come in 64-row tiles
+  return f32_ways((long long)(s.Nq / 64) * s.BH, s.Nq / 32, s);
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_t(const Shape& s, const float* Q, const float* K, const float* V, float* O,
-                 float* L, hipStream_t stream) {
-  const long long grid = (long long)((s.Nq + 127) / 128) * s.BH;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, Q,
-                     K, V, O, L, s.Nq, s.Nk, s.scale);
+                 float* L, float* ws, size_t ws_bytes, hipStream_t stream) {
+  const long long tiles = (long long)((s.Nq + 127) / 128) * s.BH;
+  int ns = fwd_f32_ways(s);
+  if (ns > 1 && (ws == nullptr || ws_bytes < fwd_workspace_bytes_f32(s))) ns = 1;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(tiles * ns)), dim3(256), 0,
+                     stream, Q, K, V, O, L, s.Nq, s.Nk, s.scale, ns, ws);
+  if (ns > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_f32_combine_kernel<D>), dim3((unsigned)tiles),
+                       dim3(256 * ((D + 31) / 32)), 0, stream, (const float*)ws, O, L, s.Nq,
+                       s.scale, ns);
+  }
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const float* Q, const float* K, const float* V, const float* O,
-                 const float* L, const float* dO, float* dQ, float* dK, float* dV,
-                 hipStream_t stream) {
+                 const float* L, const float* dO, float* dQ, float* dK, float* dV, float* ws,
+                 size_t ws_bytes, hipStream_t stream) {
   const long long grid = (long long)((s.Nk + 127) / 128 + (s.Nq + 127) / 128) * s.BH;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream, Q,
-                     K, V, O, L, dO, dQ, dK, dV, s.Nq, s.Nk, s.scale);
+  int ns = bwd_f32_ways(s);
+  const size_t split_bytes = (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * D * sizeof(float);
+  if (ns > 1 && (ws == nullptr || ws_bytes < split_bytes ||
+                 (reinterpret_cast<uintptr_t>(ws) & 15u) != 0))
+    ns = 1;
+  const long long tiles = (long long)(s.Nq / 64) * s.BH;
+  float* kvpart = ws;
+  float* qpart = ns > 1 ? ws + (size_t)tiles * ns * 2 * 64 * D : nullptr;
+  hipLaunchKernelGGL((bwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(grid * ns)), dim3(256), 0,
+                     stream, Q, K, V, O, L, dO, dQ, dK, dV, s.Nq, s.Nk, s.scale, ns, kvpart,
+                     qpart);
+  if (ns > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_f32_combine_kernel<D>), dim3((unsigned)(tiles * (3 * 64 * D / 1024))),
+                       dim3(256), 0, stream, (const float*)kvpart, (const float*)qpart, dQ, dK,
+                       dV, s.Nq, s.scale, ns);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t fwd_workspace_bytes_f32(const Shape& s) {
+  const int ns = fwd_f32_ways(s);
+  if (ns == 1) return 0;
+  const size_t xs = 16 * ((s.d + 31) / 32) + 2;  // floats per lane in a partial record
+  return (size_t)((s.Nq + 127) / 128) * s.BH * ns * xs * 256 * sizeof(float);
+}
+
+size_t bwd_split_workspace_bytes_f32(const Shape& s) {
+  // The size does not depend on the call being causal: room for either.
+  Shape c = s, n = s;
+  c.causal = true;
+  n.causal = false;
+  const int ns = std::max(bwd_f32_ways(c), bwd_f32_ways(n));
+  if (ns == 1) return 0;
+  return (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
+}
+
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
-                          float* O, float* L, hipStream_t stream) {
-#define FA_F(DD)                                                 \
-  case DD:                                                       \
-    return s.causal ? fwd_t<DD, true>(s, Q, K, V, O, L, stream)  \
-                    : fwd_t<DD, false>(s, Q, K, V, O, L, stream);
+                          float* O, float* L, float* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+#define FA_F(DD)                                                                          \
+  case DD:                                                                                \
+    return s.causal ? fwd_t<DD, true>(s, Q, K, V, O, L, workspace, workspace_bytes, stream) \
+                    : fwd_t<DD, false>(s, Q, K, V, O, L, workspace, workspace_bytes, stream);
   switch (s.d) {
     FA_F(16)
     FA_F(32)
@@ -424,11 +621,14 @@ hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const 
 
 hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           const float* O, const float* L, const float* dO, float* dQ, float* dK,
-                          float* dV, hipStream_t stream) {
-#define FA_B(DD)                                                                  \
-  case DD:                                                                        \
-    return s.causal ? bwd_t<DD, true>(s, Q, K, V, O, L, dO, dQ, dK, dV, stream)   \
-                    : bwd_t<DD, false>(s, Q, K, V, O, L, dO, dQ, dK, dV, stream);
+                          float* dV, float* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+#define FA_B(DD)                                                                      \
+  case DD:                                                                            \
+    return s.causal ? bwd_t<DD, true>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace,    \
+                                      workspace_bytes, stream)                        \
+                    : bwd_t<DD, false>(s, Q, K, V, O, L, dO, dQ, dK, dV, workspace,   \
+                                       workspace_bytes, stream);
   switch (s.d) {
     FA_B(16)
     FA_B(32)

@@ -6,6 +6,8 @@
 
 namespace fa {
 
+constexpr int kNumCUs = 256;  // MI355X
+
 struct Shape {
   int BH;     // B * H
   int Nq;     // queries per head
@@ -34,10 +36,17 @@ hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, co
                                 const void* dO, void* dQ, void* dK, void* dV,
                                 const float* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+// fp32: small grids likewise spread each workgroup's key (forward) or step (backward) range
+// over several workgroups when the workspace holds fwd_workspace_bytes_f32 or
+// bwd_split_workspace_bytes_f32 bytes; otherwise they run unsplit (fp32 needs no workspace).
+size_t fwd_workspace_bytes_f32(const Shape& s);
+size_t bwd_split_workspace_bytes_f32(const Shape& s);
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
-                          float* O, float* L, hipStream_t stream);
+                          float* O, float* L, float* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           const float* O, const float* L, const float* dO, float* dQ, float* dK,
-                          float* dV, hipStream_t stream);
+                          float* dV, float* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 }  // namespace fa
