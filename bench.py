@@ -78,7 +78,7 @@ def kernel_names(w):
     built for d = 32 and 64 only)."""
     c = "true" if w.causal else "false"
     if w.dtype == "f32":
-        return f"fwd_f32_kernel<{w.d}, {c}>", f"dkdv_f32_kernel+dq_f32_kernel<{w.d}, {c}>"
+        return f"fwd_f32_kernel<{w.d}, {c}>", f"bwd_f32_kernel<{w.d}, {c}>"
     n_cus = 256
     square = w.causal and w.Nq == w.Nk and w.Nq % 128 == 0 and w.d >= 32
     pairs = (w.Nq // 128) * w.B * w.H

@@ -42,6 +42,8 @@ def test_kernel_names_follow_dispatch():
         "fwd_causal_paired_kernel<64>", "bwd_causal_paired_kernel<64>")
     assert bench.kernel_names(WORKLOADS["xl_causal"]) == (
         "fwd_kernel<64, true>", "bwd_kernel<64, true>")
+    assert bench.kernel_names(WORKLOADS["tiny_f32"]) == (
+        "fwd_f32_kernel<16, true>", "bwd_f32_kernel<16, true>")
 
 
 def test_more_than_one_gpu_is_refused():
