@@ -116,16 +116,17 @@ def test_small_cases_match_oracle(gpu, case):
     compare(got, full_oracle(inp, causal, scale), dtype)
 
 
-def o_rounding_allowance(q, k, v, do, causal, scale):
-    """Extra gradient error that storing O in bf16 forces on D = rowsum(dO o O).
+def o_rounding_allowance(q, k, v, do, causal, scale, u=2.0 ** -8):
+    """Extra gradient error that the stored O's error forces on D = rowsum(dO o O).
 
     Problem flash_backward forms D from O, and problem flash_forward casts O to the input
-    dtype before the store, so D_i moves by up to u * sum_k |dO_ik| |O_ik| (u = 2^-8 covers
-    bf16 round-to-nearest) and dS_ij = P_ij (dP_ij - D_i) by P_ij times that. With a large
-    scale (peaked rows, dP_ij close to D_i) this dominates the gradient error.
+    dtype before the store, so with O off by a relative u (2^-8 covers bf16
+    round-to-nearest), D_i moves by up to u * sum_k |dO_ik| |O_ik| and dS_ij = P_ij (dP_ij - D_i)
+    by P_ij times that. With a large scale (peaked rows, dP_ij close to D_i) this dominates
+    the gradient error.
     """
     o, _, p = oracle.head_forward(q, k, v, causal, scale)
-    dd = 2.0 ** -8 * np.sum(np.abs(do) * np.abs(o), axis=1)
+    dd = u * np.sum(np.abs(do) * np.abs(o), axis=1)
     w = p * dd[:, None]
     return {"dQ": abs(scale) * w @ np.abs(k), "dK": abs(scale) * w.T @ np.abs(q)}
 
@@ -141,6 +142,33 @@ def test_unusual_scales(gpu, scale):
         allow = o_rounding_allowance(*a, True, scale)
         for n in ("O", "L", "dQ", "dK", "dV"):
             check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
+def test_fp32_unusual_scales(gpu, scale):
+    """fp32 on the split forward and backward (one head of 1024): a negative scale takes the
+    scores of -Q (-K in the dK/dV pass), and 0 gives uniform attention.
+
+    Tolerance: the 1e-4 absolute bound plus u |oracle|, u = 2 (1 + max|L|) 2^-24, and for dQ
+    and dK the error that an O off by a relative u forces through D (o_rounding_allowance).
+    P = exp(S scale - L) is evaluated in fp32 from an exponent formed out of terms as large
+    as |L| (about 80 at scale 2), so P, O and every output built from them carry a relative
+    error of order |L| 2^-24; with peaked rows dP - D nearly cancels and D inherits O's."""
+    from tiled_attention_causal_amd import backward_workspace_bytes, forward_workspace_bytes
+    note(f"fp32 scale {scale}")
+    inp = make_inputs(1, 1, 1024, 1024, 64, "f32", index=8150)
+    assert forward_workspace_bytes(inp["q"], inp["k"], True) > 0
+    assert backward_workspace_bytes(inp["q"], inp["k"]) > 0
+    got = run_gpu(inp, True, scale, gpu)
+    ref = full_oracle(inp, True, scale)
+    u = 2.0 * (1.0 + np.abs(ref["L"]).max()) * 2.0 ** -24
+    a = [to_f64(inp[n][0, 0]) for n in ("q", "k", "v", "do")]
+    allow = o_rounding_allowance(*a, True, scale, u=u)
+    errs = {}
+    for n in ("O", "L", "dQ", "dK", "dV"):
+        extra = u * np.abs(ref[n][0]) + allow.get(n, 0.0)
+        errs[n] = check(n, got[n][0, 0], ref[n][0], "f32", allowance=extra)
+    note(f"  max abs err {errs}")
 
 
 FULL = ["tiny_f32", "b8_n4096_d64", "gpt_small", "xl_causal", "xl_noncausal"]
