@@ -29,9 +29,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -81,30 +78,12 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, z);
-}
-
 // Eight consecutive fp32 accumulator registers -> one bf16 MFMA operand (RNE).
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& x, int base) {
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (bf16)x[base + e];
   return r;
-}
-
-// Position of row index m (0..31 inside a 32-row block pair of 16-steps) in a transposed
-// tile. An MFMA C fragment leaves, in lane group g, rows 16t + 8a + 4g + b (a in {0,1},
-// b in 0..3) of step t; storing row 16t + 8a + 4g + b at column 16t + 8g + 4a + b makes the
-// eight values a lane group needs for step t one contiguous 16-byte chunk: chunk 2t + g.
-__device__ __forceinline__ int tpos(int m) {
-  return (m & ~15) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
-// Row m of the e-th element (e = 0..7) of transposed chunk kc: inverse of tpos.
-__device__ __forceinline__ int chunk_row(int kc, int e) {
-  return 16 * (kc >> 1) + 8 * (e >> 2) + 4 * (kc & 1) + (e & 3);
 }
 
 // XOR key of row r for an LDS tile with NCH 16-byte chunks per row. With 8 chunks (64
@@ -167,13 +146,6 @@ __device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
-// Value held by lane (lane ^ 32): a VALU op, no LDS round trip. With a = b = x, lane l < 32
-// finds x[l + 32] in b and lane l >= 32 finds x[l - 32] in a.
-__device__ __forceinline__ float swap_halves(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  permlane32_swap(a, b);
-  return __builtin_bit_cast(float, (__lane_id() < 32) ? b : a);
-}
 // x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]) in every lane: after the swap a holds the lower
 // half's value and b the upper half's in every lane, so no lane select is needed and both
 // halves get the bitwise identical result.
@@ -282,13 +254,5 @@ struct Tile {
     return __builtin_bit_cast(bf16x8, ab);
   }
 };
-
-// Pack element `sel` (0 or 1) of two bf16 pairs into one pair: (a.sel, b.sel).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
-}
 
 }  // namespace fa
