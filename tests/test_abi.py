@@ -68,9 +68,9 @@ def test_workspace_sizes(lib):
     # steps are 32 rows); the size covers either.
     assert lib.fa_backward_workspace_bytes(1, 1, 1, 2048, 2048, 32) == (
         2048 * 8 + 32 * 8 * 48 * 128 * 4)
-    # d = 128 (bwd_kernel, one workgroup per CU): causal 4 ways, non-causal 2.
+    # d = 128 (bwd_kernel, two workgroups per CU): causal 8 ways, non-causal 4.
     assert lib.fa_backward_workspace_bytes(1, 1, 1, 8192, 8192, 128) == (
-        8192 * 8 + 128 * 4 * 192 * 128 * 4)
+        8192 * 8 + 128 * 8 * 192 * 128 * 4)
     assert lib.fa_backward_workspace_bytes(1, 8, 1, 8192, 8192, 128) == 8 * 8192 * 8
     assert lib.fa_backward_workspace_bytes(1, 4, 25, 2048, 1024, 128) == 100 * 2048 * 8
     assert lib.fa_backward_workspace_bytes(1, 2, 3, 0, 64, 64) == 0

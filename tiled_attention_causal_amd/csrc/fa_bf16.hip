@@ -1091,7 +1091,7 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
 // rows of dK^T and dV^T at kvpart + ((bh T + t) ns + sw) 2 * 64 D (dV^T after dK^T) and of dQ^T
 // at qpart + ((bh T + t) ns + sw) 64 D, T = N / 64; bwd_split_combine_kernel adds them up.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_kernel(const bf16* __restrict__ Q,
+__global__ __launch_bounds__(256, 2) void bwd_kernel(const bf16* __restrict__ Q,
                                                   const bf16* __restrict__ K,
                                                   const bf16* __restrict__ V,
                                                   const float* __restrict__ L2,
@@ -1434,16 +1434,15 @@ bool bwd_uses_paired(const Shape& s) {
 // Workgroups per workgroup of the split backward (Nq = Nk, a multiple of 128). Small grids
 // spread each workgroup's steps over up to 8 workgroups, doubling while every share keeps at
 // least kMinShare steps and the grid stays within the CUs' room for the kernel's workgroups
-// (two per CU for the paired kernel and bwd_kernel at d <= 64, one for bwd_kernel at d = 128).
-// Causal bwd_kernel grids may take twice that: their shares differ in length, and dispatched
-// longest first, the short dK/dV shares free their CUs for the long dQ ones.
+// (two per CU for either kernel). Causal bwd_kernel grids may take twice that: their shares
+// differ in length, and dispatched longest first, the short dK/dV shares free their CUs for
+// the long dQ ones.
 constexpr int kMinShare = 8;
 int bwd_split_ways(const Shape& s) {
   if (s.Nq != s.Nk || s.Nq % 128 != 0) return 1;
   const bool paired = bwd_uses_paired(s);
   const long long wgs = (long long)(s.Nq / 64) * s.BH;  // either kernel: N / 64 per head
-  const long long room = (long long)kNumCUs * (paired || s.d <= 64 ? 2 : 1) *
-                         (!paired && s.causal ? 2 : 1);
+  const long long room = (long long)kNumCUs * 2 * (!paired && s.causal ? 2 : 1);
   const int steps = paired ? s.Nq / 64 + 1 : s.Nq / 32;  // the longest workgroup's steps
   int ns = 1;
   while (ns < 8 && wgs * ns * 2 <= room && steps / (ns * 2) >= kMinShare) ns *= 2;
