@@ -70,27 +70,27 @@ def source_digest() -> str:
 
 
 def kernel_names(w):
-    """Names of the forward and backward kernels the library launches for workload `w`
-    following the dispatch rules of fa_bf16.hip and fa_f32.hip: the paired (split, for
-    d <= 64 in the forward) causal kernels serve square causal grids of 128-row tiles that fit
-    the chip in one wave of workgroups; at d <= 64 the paired kernels also take grids of up
-    to two (forward) or three (backward) of their workgroups per CU (the backward pairing is
-    built for d = 32 and 64 only)."""
+    """Names of the main forward and backward kernels the library launches for workload `w`,
+    following the dispatch rules of fa_bf16.hip and fa_f32.hip. Square causal grids of
+    128-row tiles that fit the chip in one wave of workgroups take the split forward
+    (d <= 64) or the paired forward (d = 128); at d = 32 and 64 the paired kernels also take
+    grids of up to two (forward) or three (backward) of their workgroups per CU."""
     c = "true" if w.causal else "false"
     if w.dtype == "f32":
         return f"fwd_f32_kernel<{w.d}, {c}>", f"bwd_f32_kernel<{w.d}, {c}>"
     n_cus = 256
-    square = w.causal and w.Nq == w.Nk and w.Nq % 128 == 0 and w.d >= 32
+    square = w.causal and w.Nq == w.Nk and w.Nq % 128 == 0
+    paired_d = 32 <= w.d <= 64
     pairs = (w.Nq // 128) * w.B * w.H
     if square and pairs <= n_cus:
         fwd = (f"fwd_causal_split_kernel<{w.d}>" if w.d <= 64
                else f"fwd_causal_paired_kernel<{w.d}>")
-    elif square and w.d <= 64 and pairs <= 2 * n_cus:
+    elif square and paired_d and pairs <= 2 * n_cus:
         fwd = f"fwd_causal_paired_kernel<{w.d}>"
     else:
         fwd = f"fwd_kernel<{w.d}, {c}>"
     bwd = (f"bwd_causal_paired_kernel<{w.d}>"
-           if square and w.d <= 64 and (w.Nq // 64) * w.B * w.H <= 3 * n_cus
+           if square and paired_d and (w.Nq // 64) * w.B * w.H <= 3 * n_cus
            else f"bwd_kernel<{w.d}, {c}>")
     return fwd, bwd
 

@@ -11,7 +11,7 @@ import torch
 
 import bench
 import oracle
-from seeded_inputs import WORKLOADS, make_inputs, to_f64
+from seeded_inputs import WORKLOADS, Workload, make_inputs, to_f64
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -44,6 +44,9 @@ def test_kernel_names_follow_dispatch():
         "fwd_kernel<64, true>", "bwd_kernel<64, true>")
     assert bench.kernel_names(WORKLOADS["tiny_f32"]) == (
         "fwd_f32_kernel<16, true>", "bwd_f32_kernel<16, true>")
+    one_head_d16 = Workload("one_head_d16", 99, 1, 1, 8192, 8192, 16, "bf16", True)
+    assert bench.kernel_names(one_head_d16) == (
+        "fwd_causal_split_kernel<16>", "bwd_kernel<16, true>")
 
 
 def test_more_than_one_gpu_is_refused():
