@@ -480,13 +480,16 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   const float cs = fabsf(scale);
   const float c = exp2_coef(scale);
 
-  bf16x8 qfA[DS], qfB[DS];
-  load_frags<D>(qfA, Qr, 64 * tA + 32 * wp + l32, g);
+  // qf holds the query tile of the current step: the run's first tile, then B's rows, copied
+  // in once where the run crosses from A into B (a per-step select would cost DS * 4 VALU
+  // instructions every step).
+  bf16x8 qf[DS], qfB[DS];
+  load_frags<D>(qf, Qr, 64 * (st < nA ? tA : tB) + 32 * wp + l32, g);
   load_frags<D>(qfB, Qr, 64 * tB + 32 * wp + l32, g);
   if (neg)
 #pragma unroll
     for (int q = 0; q < DS; ++q) {
-      qfA[q] = negate(qfA[q]);
+      qf[q] = negate(qf[q]);
       qfB[q] = negate(qfB[q]);
     }
 
@@ -539,7 +542,6 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
     if (act) {
       const bool isA = n < nA;
       const int qt = isA ? tA : tB, kt = isA ? n : n - nA;
-      const bf16x8(&qf)[DS] = isA ? qfA : qfB;
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -561,6 +563,8 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
         for (int db = 0; db < DB; ++db) o[db] = zero16();
         m = 0.f;
         l = 0.f;
+#pragma unroll
+        for (int q = 0; q < DS; ++q) qf[q] = qfB[q];
       }
     }
     wait_vmem();
