@@ -38,8 +38,8 @@ KERNEL_SOURCES = ["tiled_attention_causal_amd/csrc/fa_bf16.hip",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -511,7 +511,7 @@ def main():
 
     if args.all:
         for name, ww in WORKLOADS.items():
-            rr = time_workload(ww, max(5, args.steps // 5), 3)
+            rr = time_workload(ww, max(5, args.steps // 5), max(3, args.warmup // 5))
             f2 = ww.counted_flops()
             print(f"{name:18s} fwd {rr['fwd_ms_median']:.4f} ms "
                   f"({f2['fwd'] / rr['fwd_ms_median'] / 1e9:.1f} TF/s)  bwd "

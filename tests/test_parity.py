@@ -373,6 +373,44 @@ def test_fp32_split_over_workgroups_matches_oracle(gpu, case):
     compare(got, full_oracle(inp, causal, scale, heads), "f32", heads)
 
 
+# Square causal grids too short to split (no forward workspace): the split kernel at d = 16
+# and the paired kernel at d = 128 run one share per tile pair and store O and L themselves,
+# without the merge launch.
+ONE_SHARE = [(1, 1, 512, 16), (1, 2, 512, 128)]
+
+
+@pytest.mark.parametrize("case", ONE_SHARE, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_small_grid_forward_single_share(gpu, case):
+    from bench import kernel_names
+    from tiled_attention_causal_amd import forward_workspace_bytes
+    B, H, N, d = case
+    note(f"single-share small-grid forward case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=9700 + N + d + H)
+    assert forward_workspace_bytes(inp["q"], inp["k"], True) == 0
+    fwd, _ = kernel_names(Workload("case", 0, B, H, N, N, d, "bf16", True))
+    assert fwd == ("fwd_causal_split_kernel<16>" if d == 16 else "fwd_causal_paired_kernel<128>")
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    compare(got, full_oracle(inp, True, scale), "bf16")
+
+
+# fp32 causal grids with Nq != Nk (ragged tiles) that are small enough for the forward to
+# spread each query tile's keys over several workgroups.
+F32_RAGGED_SPLIT = [(1, 1, 1000, 1500, 64), (1, 2, 1500, 700, 32)]
+
+
+@pytest.mark.parametrize("case", F32_RAGGED_SPLIT, ids=lambda c: "B{}H{}q{}k{}d{}".format(*c))
+def test_fp32_split_forward_ragged_causal(gpu, case):
+    from tiled_attention_causal_amd import forward_workspace_bytes
+    B, H, Nq, Nk, d = case
+    note(f"fp32 ragged causal split case {case}")
+    inp = make_inputs(B, H, Nq, Nk, d, "f32", index=9800 + Nq + d + H)
+    assert forward_workspace_bytes(inp["q"], inp["k"], True) > 0
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    compare(got, full_oracle(inp, True, scale), "f32")
+
+
 @pytest.mark.parametrize("d,causal", [(64, True), (128, True), (64, False)])
 def test_backward_minimum_workspace_matches_split(gpu, d, causal):
     """A workspace of only the per-row terms: the same grid runs unsplit, which changes only
