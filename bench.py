@@ -148,29 +148,55 @@ def time_workload(w, steps, warmup):
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
 
-    # Per-launch durations with events on the stream the kernels run on. The backward is
-    # issued as its two steps (fa_backward_preprocess, then fa_backward_main: exactly what
-    # fa_backward enqueues) so that its main kernel is timed on its own.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # Per-launch durations with HIP events on the stream the kernels run on. Each of the
+    # step's three launches (fa_forward, then fa_backward as its two steps
+    # fa_backward_preprocess and fa_backward_main, exactly what fa_backward enqueues) is
+    # repeated back to back between two events, in chunks of CHUNK launches, until `steps`
+    # launches of each are timed; a chunk's elapsed time over CHUNK is the kernel's average
+    # launch duration. The launches go through the C ABI with their arguments marshalled
+    # once, so the host keeps ahead of even the 4 us preprocessing kernel and the events
+    # time the GPU, not the host's launch rate.
+    from tiled_attention_causal_amd import _lib
+    lib = _lib.load()
+    dt = _lib.FA_DTYPE_BF16 if w.dtype == "bf16" else _lib.FA_DTYPE_F32
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    sp = stream.cuda_stream
+    causal = int(bool(w.causal))
+    fa = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), causal, w.scale,
+          o.data_ptr(), lse.data_ptr(), fws.data_ptr() if fws.numel() else None, fws.numel(),
+          sp)
+    pa = (dt, B, H, Nq, d, o.data_ptr(), lse.data_ptr(), do.data_ptr(), ws.data_ptr(),
+          ws.numel(), sp)
+    ma = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+          lse.data_ptr(), do.data_ptr(), causal, w.scale, dq.data_ptr(), dk.data_ptr(),
+          dv.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+    launches = [(lib.fa_forward, fa), (lib.fa_backward_preprocess, pa),
+                (lib.fa_backward_main, ma)]
+    CHUNK = 20
+    nchunks = max(1, steps // CHUNK)
+    per = [[] for _ in launches]
     torch.cuda.synchronize(dev)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse, workspace=fws)
-        ev[i][1].record(stream)
-        fa_backward_preprocess(o, lse, do, ws)
-        ev[i][2].record(stream)
-        fa_backward_main(q, k, v, o, lse, do, w.causal, w.scale, ws, dq=dq, dk=dk, dv=dv)
-        ev[i][3].record(stream)
+    for _ in range(nchunks):
+        for i, (fn, a) in enumerate(launches):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(CHUNK):
+                st = fn(*a)
+                if st != _lib.FA_SUCCESS:
+                    raise _lib.FAError(st, fn.__name__)
+            e1.record(stream)
+            per[i].append((e0, e1))
     torch.cuda.synchronize(dev)
 
-    def stat(a, b):
-        t = sorted(e[a].elapsed_time(e[b]) for e in ev)
-        return sum(t) / steps, t[steps // 2]
+    def stat(i):
+        t = sorted(a.elapsed_time(b) / CHUNK for a, b in per[i])
+        return sum(t) / len(t), t[len(t) // 2]
 
-    fwd_mean, fwd_med = stat(0, 1)
-    prep_mean, _ = stat(1, 2)
-    main_mean, _ = stat(2, 3)
-    bwd_mean, bwd_med = stat(1, 3)
+    (fwd_mean, fwd_med), (prep_mean, prep_med), (main_mean, main_med) = (
+        stat(0), stat(1), stat(2))
+    bwd_mean, bwd_med = prep_mean + main_mean, prep_med + main_med
     return {
         "ms_per_step": wall * 1e3 / steps,
         "fwd_ms_mean": fwd_mean,
