@@ -919,17 +919,24 @@ template <int D>
 struct QRow {
   bf16x8 qf[D / 16], dof[D / 16];
   float l2, nd;
-  __device__ __forceinline__ void load(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr, int qrow,
-                                       int g, int neg) {
-    constexpr int DS = D / 16;
+  // Issues the loads; finish() (after they have landed) applies the sign.
+  __device__ __forceinline__ void issue(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr,
+                                        int qrow, int g) {
     load_frags<D>(qf, Qr, qrow, g);
     load_frags<D>(dof, dOr, qrow, g);
     l2 = buf_load_f32(L2r, qrow * 4);
     nd = buf_load_f32(NDr, qrow * 4);
-    wait_vmem();
+  }
+  __device__ __forceinline__ void finish(int neg) {
     if (neg)
 #pragma unroll
-      for (int s = 0; s < DS; ++s) qf[s] = negate(qf[s]);
+      for (int s = 0; s < D / 16; ++s) qf[s] = negate(qf[s]);
+  }
+  __device__ __forceinline__ void load(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr, int qrow,
+                                       int g, int neg) {
+    issue(Qr, dOr, L2r, NDr, qrow, g);
+    wait_vmem();
+    finish(neg);
   }
 };
 
@@ -1142,13 +1149,18 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(const bf16* __restrict__ Q,
 // reads of `cur` do not alias the loads in flight into the other two buffers, and inserts no
 // wait for them. A step that issues other vector-memory instructions must wait for all of
 // them itself before returning.
-template <int KEEP, class Fetch, class Step>
+//
+// ready() runs once after the first two tiles' loads have landed and before the first step:
+// the caller issues its own first loads (stationary fragments) ahead of the call, so they
+// share that one memory round trip, and finishes them in ready().
+template <int KEEP, class Fetch, class Step, class Ready>
 __device__ __forceinline__ void stream3(int first, int last, bf16* __restrict__ b0,
                                         bf16* __restrict__ b1, bf16* __restrict__ b2,
-                                        Fetch&& fetch, Step&& step) {
+                                        Fetch&& fetch, Step&& step, Ready&& ready) {
   if (first < last) fetch(first, b0);
   if (first + 1 < last) fetch(first + 1, b1);
   wait_vmem();
+  ready();
   __syncthreads();
   auto one = [&](int n, bf16* cur, bf16* pre) {
     const bool more = n + 2 < last;
@@ -1232,7 +1244,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     int kt = (pr == 1 && n_lo < nB) ? tB + 0 : tA + 0;
     int krow = 64 * kt + 32 * wp + l32;
     bf16x8 kf[DS], vf[DS];
-    load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
+    load_frags<D>(kf, Kr, krow, g);  // lands with the first two tiles (stream3's ready)
+    load_frags<D>(vf, Vr, krow, g);
     f32x16 dvt[DB], dkt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -1270,6 +1283,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
             krow = 64 * kt + 32 * wp + l32;
             load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);  // waits for all its loads
           }
+        },
+        [&] {
+          if (neg)
+#pragma unroll
+            for (int s = 0; s < DS; ++s) kf[s] = negate(kf[s]);
         });
     // Pair 1 holds A's partial sums unless its A range was empty (n == nB at the end). The
     // merge record is component-major (component k of wave wp's lane at k * 128 + wp * 64 +
@@ -1329,7 +1347,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     int qt = (pr == 1 && n_lo < nB) ? tB + 0 : tA + 0;  // as kt above
     int qrow = 64 * qt + 32 * wp + l32;
     QRow<D> row;
-    row.load(Qr, dOr, L2r, NDr, qrow, g, neg);
+    row.issue(Qr, dOr, L2r, NDr, qrow, g);  // lands with the first two tiles (stream3's ready)
     f32x16 dqt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = zero16();
@@ -1361,7 +1379,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
             qrow = 64 * qt + 32 * wp + l32;
             row.load(Qr, dOr, L2r, NDr, qrow, g, neg);  // waits for all its loads
           }
-        });
+        },
+        [&] { row.finish(neg); });
     const bool p1_has_A = n_hi > nB;
     if (ns > 1 && pr == 1) {  // as for dK/dV above
       if (n_lo >= nB)
