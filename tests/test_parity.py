@@ -306,6 +306,37 @@ def test_forward_split_over_workgroups_matches_oracle(gpu, case):
     compare(got, full_oracle(inp, True, scale, heads), "bf16", heads)
 
 
+# The forward's online softmax rescales a row only when its max grows by more than 8 in
+# exp2 units (the lazy rescale). Keys whose norm grows along the sequence, at scale 1, make
+# the later tiles' scores exceed the earlier tiles' max by far more than that, so the split
+# forward rescales on most steps (one share per tile pair, and four).
+GROWING = [(1, 2, 1024, 64), (1, 1, 4096, 64)]
+
+
+@pytest.mark.parametrize("case", GROWING, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_split_forward_growing_scores(gpu, case):
+    B, H, N, d = case
+    note(f"growing-score split forward case {case}")
+    inp = make_inputs(B, H, N, N, d, "bf16", index=9900 + N + H)
+    ramp = (1.0 + 4.0 * torch.arange(N, dtype=torch.float32) / N).view(1, 1, N, 1)
+    inp["k"] = (inp["k"].float() * ramp).to(torch.bfloat16).contiguous()
+    scale = 1.0
+    q, k = to_f64(inp["q"][0, 0]), to_f64(inp["k"][0, 0])
+    s = (q @ k.T) * scale * np.log2(np.e)
+    first = s[64:, :64].max(axis=1)
+    later = np.array([s[i, 64:i + 1].max() for i in range(64, N)])
+    assert np.mean(later - first > 8) > 0.5  # most rows rescale after their first tile
+    got = run_gpu(inp, True, scale, gpu)
+    ref = full_oracle(inp, True, scale)
+    # Peaked rows: the gradients carry the error that O's bf16 rounding forces through D
+    # (o_rounding_allowance, as for the large scales above); O and L carry none.
+    for h in range(H):
+        a = [to_f64(inp[n][0, h]) for n in ("q", "k", "v", "do")]
+        allow = o_rounding_allowance(*a, True, scale)
+        for n in ("O", "L", "dQ", "dK", "dV"):
+            check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
+
+
 # Grids between one and two tile pairs per CU: the forward takes the four-wave paired kernel
 # (two per CU), the backward the paired kernel (up to three per CU).
 MID = [(4, 9, 1024, 32), (2, 17, 1024, 64)]
