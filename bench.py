@@ -7,7 +7,8 @@ in HBM before the timed region starts. Counted work (the metric's convention): f
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Prints one JSON line. Extra modes:
+The defaults (W = 500, K = 2000) let the GPU reach its steady clock first: the first hundred
+or so steps of this work run 10-25% slower. Prints one JSON line. Extra modes:
     --copy-calibration   run only a plain device copy of known size (HBM counter scaling)
     --all                also print a per-workload table to stderr
     --sweep              forward / backward / end-to-end latency of these kernels against
