@@ -16,6 +16,8 @@ or so steps of this work run 10-25% slower. Prints one JSON line. Extra modes:
                          (a markdown table on stdout, no JSON line)
     --e2e                training steps of a toy decoder with plain attention, then with the
                          flash kernels monkey-patched in as its attention (two JSON lines)
+    --atomic-dq          the backward with dQ from fp32 atomics against the deterministic
+                         two-pass split, on --workload (one JSON line)
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--e2e", action="store_true",
                     help="training-step time of a toy decoder, plain vs flash attention")
+    ap.add_argument("--atomic-dq", action="store_true",
+                    help="backward time with dQ from fp32 atomics against the two-pass split")
     ap.add_argument("--sweep-n", default="128,256,512,1024,2048,4096,8192")
     ap.add_argument("--sweep-d", default="16,32,64,128")
     ap.add_argument("--sweep-dtypes", default="bf16,f32")
@@ -451,6 +455,52 @@ def toy_model(d_model, n_heads, d_ff, n_layers, dtype, device, seed=0):
     return torch.nn.Sequential(*[Block() for _ in range(n_layers)])
 
 
+def atomic_dq(args):
+    """The two dQ strategies of "Systems and Parallelism" (CS336 field map, A2), section
+    1.3.3, on one workload: fa_backward (two-pass split, deterministic) and
+    fa_backward_atomic (dQ from fp32 atomic additions), each launched back to back between
+    HIP events after a warm-up, the median of five chunks of `steps // 5` launches."""
+    import torch
+    from seeded_inputs import WORKLOADS, workload_inputs
+    from tiled_attention_causal_amd import (backward_atomic_workspace_bytes,
+                                            backward_workspace_bytes, fa_backward,
+                                            fa_backward_atomic, fa_forward)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = workload_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, w.causal, w.scale)
+    ws = torch.empty(max(backward_workspace_bytes(q, k), backward_atomic_workspace_bytes(q, k)),
+                     dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    runs = {
+        "two_pass": lambda: fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk,
+                                        dv=dv, workspace=ws),
+        "atomic": lambda: fa_backward_atomic(q, k, v, o, lse, do, w.causal, w.scale, dq=dq,
+                                             dk=dk, dv=dv, workspace=ws),
+    }
+    for _ in range(max(1, args.warmup // 4)):
+        for fn in runs.values():
+            fn()
+    torch.cuda.synchronize(dev)
+    chunk = max(1, args.steps // 5)
+    out = {}
+    for name, fn in runs.items():
+        t = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(chunk):
+                fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1) / chunk)
+        ms = sorted(t)[2]
+        out[name] = {"bwd_ms": round(ms, 5),
+                     "bwd_tflops": round(w.counted_flops()["bwd"] / (ms * 1e-3) / 1e12, 2)}
+    print(json.dumps({"atomic_dq": out, "workload": w.name, "deterministic": "two_pass"}))
+
+
 def e2e(args):
     """Training steps of the toy decoder (forward, backward, AdamW) with plain attention and
     then with the flash kernels patched in as its attention function."""
@@ -526,6 +576,9 @@ def main():
         return
     if args.e2e:
         e2e(args)
+        return
+    if args.atomic_dq:
+        atomic_dq(args)
         return
 
     w = WORKLOADS[args.workload]

@@ -187,6 +187,35 @@ FA_API fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t 
                            float scale, void* dQ, void* dK, void* dV, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * fa_backward_atomic_workspace_bytes -- bytes of device workspace fa_backward_atomic needs
+ * (0 for fp32 and for sizes it would reject): the two per-row floats of fa_backward, then an
+ * fp32 dQ accumulator, B * H * Nq * (2 + d) * 4 bytes in all.
+ */
+FA_API size_t fa_backward_atomic_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H,
+                                                 int64_t Nq, int64_t Nk, int64_t d);
+
+/*
+ * fa_backward_atomic -- fa_backward with the other dQ strategy of section 1.3.3: dQ is
+ * accumulated with fp32 atomic additions instead of a second pass over the key tiles.
+ * After the same preprocessing step, only the dK/dV workgroups run (128 keys each); for
+ * every visible 32-row query tile each wave forms its keys' share dS K on the matrix cores
+ * and adds it into an fp32 accumulator in the workspace, which a last launch scales and
+ * rounds into dQ. Since the order of the atomic additions varies, dQ may differ from run to
+ * run in its last bits (dK and dV do not); fa_backward is the deterministic choice.
+ *
+ * bf16 only: fp32 returns FA_ERROR_NOT_SUPPORTED. Arguments as for fa_backward, except
+ * that workspace_bytes must be at least fa_backward_atomic_workspace_bytes() (else
+ * FA_ERROR_INVALID_VALUE). Four launches on `stream`: preprocessing, zeroing of the
+ * accumulator, main, conversion.
+ */
+FA_API fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                    int64_t Nk, int64_t d, const void* Q, const void* K,
+                                    const void* V, const void* O, const float* L,
+                                    const void* dO, int is_causal, float scale, void* dQ,
+                                    void* dK, void* dV, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* fa_status_string -- static, NUL-terminated name of a status code (never NULL). */
 FA_API const char* fa_status_string(fa_status status);
 

@@ -28,9 +28,10 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_symbols() == ["fa_backward", "fa_backward_main", "fa_backward_preprocess",
-                                  "fa_backward_workspace_bytes", "fa_forward",
-                                  "fa_forward_workspace_bytes", "fa_status_string"]
+    assert declared_symbols() == ["fa_backward", "fa_backward_atomic",
+                                  "fa_backward_atomic_workspace_bytes", "fa_backward_main",
+                                  "fa_backward_preprocess", "fa_backward_workspace_bytes",
+                                  "fa_forward", "fa_forward_workspace_bytes", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -213,3 +214,34 @@ def test_signature_table_matches_header_argument_counts():
         m = re.search(r"FA_API[\w\s\*]+?\b" + name + r"\s*\(([^)]*)\)", text)
         nargs = len([a for a in m.group(1).split(",") if a.strip()])
         assert nargs == len(_lib.SIGNATURES[name][1]), name
+
+
+def bwd_atomic(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
+               causal=1, scale=0.125, dq=P, dk=P, dv=P, ws=P, ws_bytes=1 << 30):
+    return lib.fa_backward_atomic(dtype, B, H, Nq, Nk, d, q, k, v, o, lse, do, causal, scale,
+                                  dq, dk, dv, ws, ws_bytes, None)
+
+
+def test_atomic_workspace_sizes(lib):
+    # Two per-row floats, then the fp32 dQ accumulator: B*H*Nq*(2 + d)*4 bytes; bf16 only.
+    assert lib.fa_backward_atomic_workspace_bytes(1, 8, 1, 4096, 4096, 64) == 8 * 4096 * 66 * 4
+    assert lib.fa_backward_atomic_workspace_bytes(1, 2, 3, 100, 300, 16) == 6 * 100 * 18 * 4
+    assert lib.fa_backward_atomic_workspace_bytes(0, 8, 1, 4096, 4096, 64) == 0
+    assert lib.fa_backward_atomic_workspace_bytes(1, 8, 1, 4096, 4096, 48) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 2), (dict(dtype=5), 2), (dict(d=24), 2), (dict(Nk=0), 1),
+    (dict(q=None), 1), (dict(dq=None), 1), (dict(dk=BAD), 1), (dict(scale=math.nan), 1),
+    (dict(ws=None), 1),
+    (dict(ws_bytes=128 * 8), 1),             # enough for fa_backward, not for the accumulator
+    (dict(ws_bytes=128 * 66 * 4 - 1), 1),
+])
+def test_backward_atomic_rejects(lib, kw, code):
+    assert bwd_atomic(lib, **kw) == code
+
+
+def test_backward_atomic_empty_is_a_noop(lib):
+    assert bwd_atomic(lib, B=0) == 0
+    assert bwd_atomic(lib, Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None,
+                      dq=None, dk=None, dv=None) == 0

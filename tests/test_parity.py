@@ -528,3 +528,82 @@ def test_preprocess_then_main_equals_backward(gpu, case):
     torch.cuda.synchronize(gpu)
     for name, a, b in zip(("dQ", "dK", "dV"), got, want):
         assert torch.equal(a, b), name
+
+
+# fa_backward_atomic: dQ from fp32 atomic additions by the dK/dV workgroups alone (the
+# other dQ strategy of section 1.3.3). Ragged tails, Nq != Nk, every head dimension, causal
+# and not.
+ATOMIC = [
+    (1, 2, 200, 200, 64, True),
+    (2, 1, 333, 333, 32, False),
+    (1, 1, 257, 129, 128, True),
+    (1, 1, 100, 300, 16, True),
+    (1, 2, 1024, 1024, 64, True),
+    (1, 1, 520, 520, 128, False),
+]
+
+
+def run_gpu_atomic(inp, causal, scale, dev):
+    from tiled_attention_causal_amd import fa_backward_atomic, fa_forward
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, causal, scale)
+    dq, dk, dv = fa_backward_atomic(q, k, v, o, lse, do, causal, scale)
+    torch.cuda.synchronize(dev)
+    return {"O": o.cpu(), "L": lse.cpu(), "dQ": dq.cpu(), "dK": dk.cpu(), "dV": dv.cpu()}
+
+
+@pytest.mark.parametrize("case", ATOMIC, ids=lambda c: "B{}H{}q{}k{}d{}{}".format(
+    *c[:5], "causal" if c[5] else "full"))
+def test_atomic_backward_matches_oracle(gpu, case):
+    B, H, Nq, Nk, d, causal = case
+    note(f"atomic backward case {case}")
+    inp = make_inputs(B, H, Nq, Nk, d, "bf16", index=9950 + Nq + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu_atomic(inp, causal, scale, gpu)
+    compare(got, full_oracle(inp, causal, scale), "bf16")
+
+
+def test_atomic_backward_negative_scale(gpu):
+    note("atomic backward, scale -0.3")
+    inp = make_inputs(1, 2, 160, 160, 64, "bf16", index=8100)
+    got = run_gpu_atomic(inp, True, -0.3, gpu)
+    ref = full_oracle(inp, True, -0.3)
+    for h in range(2):
+        a = [to_f64(inp[n][0, h]) for n in ("q", "k", "v", "do")]
+        allow = o_rounding_allowance(*a, True, -0.3)
+        for n in ("dQ", "dK", "dV"):
+            check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
+
+
+def test_atomic_backward_agrees_with_two_pass_on_b8(gpu):
+    """On the benchmark workload (8 heads of 4096, d = 64, causal) the atomic path's dK and
+    dV come from the same per-step arithmetic as the two-pass path's, in another order of
+    the per-step sums, and its dQ from the same dS in another order: all three agree with
+    the two-pass results to bf16 rounding."""
+    from tiled_attention_causal_amd import fa_backward, fa_backward_atomic, fa_forward
+    w = WORKLOADS["b8_n4096_d64"]
+    note(f"atomic vs two-pass on {w}")
+    inp = workload_inputs(w)
+    q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, True, w.scale)
+    ref = fa_backward(q, k, v, o, lse, do, True, w.scale)
+    got = fa_backward_atomic(q, k, v, o, lse, do, True, w.scale)
+    torch.cuda.synchronize(gpu)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        a, b = a.float(), b.float()
+        err = (a - b).abs()
+        assert torch.all(err <= 2 ** -7 * b.abs() + 2e-3), (name, float(err.max()))
+
+
+def test_atomic_backward_empty_queries(gpu):
+    from tiled_attention_causal_amd import fa_backward_atomic
+    q = torch.zeros(1, 1, 0, 64, dtype=torch.bfloat16, device=gpu)
+    k = torch.randn(1, 1, 96, 64, device=gpu).to(torch.bfloat16)
+    v = torch.randn(1, 1, 96, 64, device=gpu).to(torch.bfloat16)
+    o, do = torch.zeros_like(q), torch.zeros_like(q)
+    lse = torch.zeros(1, 1, 0, dtype=torch.float32, device=gpu)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    fa_backward_atomic(q, k, v, o, lse, do, False, 0.125, dk=dk, dv=dv)
+    torch.cuda.synchronize(gpu)
+    assert torch.all(dk == 0) and torch.all(dv == 0)

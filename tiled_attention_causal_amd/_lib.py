@@ -32,6 +32,11 @@ SIGNATURES = {
     "fa_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                    _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float, _ptr, _ptr,
                                    _ptr, _ptr, ctypes.c_size_t, _ptr]),
+    "fa_backward_atomic_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64, _i64, _i64,
+                                                             _i64]),
+    "fa_backward_atomic": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr,
+                                          _ptr, _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float,
+                                          _ptr, _ptr, _ptr, _ptr, ctypes.c_size_t, _ptr]),
     "fa_backward_preprocess": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr,
                                               _ptr, _ptr, ctypes.c_size_t, _ptr]),
     "fa_backward_main": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr,

@@ -195,4 +195,32 @@ fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t 
                           dV, workspace, workspace_bytes, stream);
 }
 
+size_t fa_backward_atomic_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                          int64_t Nk, int64_t d) {
+  fa::Shape s;
+  if (dtype != FA_DTYPE_BF16 || check_common(dtype, B, H, Nq, Nk, d, 1.f, 0, &s) != FA_SUCCESS)
+    return 0;
+  return fa::bwd_atomic_workspace_bytes_bf16(s);
+}
+
+fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                             int64_t d, const void* Q, const void* K, const void* V,
+                             const void* O, const float* L, const void* dO, int is_causal,
+                             float scale, void* dQ, void* dK, void* dV, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  fa::Shape s;
+  bool nothing = false;
+  fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale,
+                                dQ, dK, dV, workspace, workspace_bytes, &s, &nothing);
+  if (st != FA_SUCCESS || nothing) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;
+  if (workspace_bytes < fa::bwd_atomic_workspace_bytes_bf16(s)) return FA_ERROR_INVALID_VALUE;
+  st = fa_backward_preprocess(dtype, B, H, Nq, d, O, L, dO, workspace, workspace_bytes, stream);
+  if (st != FA_SUCCESS) return st;
+  const hipError_t e =
+      fa::launch_bwd_atomic_bf16(s, Q, K, V, dO, dQ, dK, dV, static_cast<float*>(workspace),
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
 }  // extern "C"

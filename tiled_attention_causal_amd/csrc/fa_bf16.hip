@@ -789,13 +789,17 @@ struct KvOps {
 // register r = query 8(r/4) + 4g + r%4; P = exp2(S c - L2), dS = P (dP - D); then
 // dV^T += dO^T P and dK^T += Q^T dS (lane = key, register = column of d). When `masked`,
 // queries with offset 8(r/4) + r%4 below `lim` (earlier than this lane's key) get P = dS = 0.
-template <int D, bool EARLY>
+//
+// With DSOUT, dS (bf16, as the dK product takes it) is also written to dsT, a 32 x 32 LDS
+// tile of this wave (Tile<32, 32> layout, row = key, column = query), for a dQ product.
+template <int D, bool EARLY, bool DSOUT = false>
 __device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
                                         const bf16x8 (&kf)[D / 16],
                                         const bf16x8 (&vf)[D / 16],
                                         f32x16 (&dvt)[(D + 31) / 32],
                                         f32x16 (&dkt)[(D + 31) / 32], float c, bool masked,
-                                        int lim, int lane, int l32, int g) {
+                                        int lim, int lane, int l32, int g,
+                                        bf16* dsT = nullptr) {
   using B = Bwd<D>;
   constexpr int DS = D / 16, DB = (D + 31) / 32;
   bf16x8 qa[DS], da[DS];
@@ -840,6 +844,14 @@ __device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
   for (int st = 0; st < 2; ++st) {
     const bf16x8 pf = to_bf16x8(sp, 8 * st);
     const bf16x8 sf = to_bf16x8(dp, 8 * st);
+    if constexpr (DSOUT) {
+      // sf holds queries 16 st + 4g + 0..3 (elements 0..3) and 16 st + 8 + 4g + 0..3 (4..7)
+      // of key l32: two 8-byte pieces of row l32, in chunks 2 st and 2 st + 1.
+      const u32x4 u = __builtin_bit_cast(u32x4, sf);
+      const u32x2 lo = {u[0], u[1]}, hi = {u[2], u[3]};
+      *reinterpret_cast<u32x2*>(dsT + swz<4>(l32, 2 * st) + 4 * g) = lo;
+      *reinterpret_cast<u32x2*>(dsT + swz<4>(l32, 2 * st + 1) + 4 * g) = hi;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       if constexpr (EARLY) {
@@ -1138,6 +1150,133 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(const bf16* __restrict__ Q,
     dq_part<D, CAUSAL>(smem, Qr, Kr, Vr, L2r, NDr, dOr, dQ + oq, it * 128, Nq, Nk, scale, neg,
                        sw, ns, ns > 1 ? qpart + head_part : nullptr);
   }
+}
+
+// Backward with dQ accumulated atomically: the nondeterministic alternative to the two-pass
+// split ("Systems and Parallelism" (CS336 field map, A2), section 1.3.3, names both). Only the
+// dK/dV kind of workgroup runs: 128 keys each (four waves of 32), walking the visible 32-row
+// query tiles as dkdv_part does. Each wave also stages its dS (bf16, transposed) in LDS and
+// forms its keys' share of the tile's dQ, dS K, on the matrix cores; the four shares are
+// summed in LDS and added into the fp32 accumulator dqacc ([B, H, Nq, d], zeroed beforehand)
+// with hardware float atomics; dq_convert_kernel then scales and rounds it. The order of
+// the additions, and so dQ's last bits, vary from run to run.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_atomic_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const float* __restrict__ L2, const float* __restrict__ ND, const bf16* __restrict__ dO,
+    float* __restrict__ dqacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int Nq, int Nk,
+    float scale, int neg) {
+  using B = Bwd<D>;
+  using DTile = Tile<32, 32>;
+  constexpr int DS = B::DS, DB = B::DB;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * B::KV_BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 ktile[4][B::T];        // a wave's 32 keys
+  __shared__ __attribute__((aligned(1024))) bf16 dstile[4][DTile::ELEMS];  // a wave's dS^T
+  __shared__ __attribute__((aligned(16))) float red[4][32 * D];  // the waves' dQ shares
+  const int nkv = (Nk + 127) / 128;
+  const int bh = blockIdx.x / nkv, k0 = (blockIdx.x % nkv) * 128;
+  const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
+  const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
+  const rsrc_t Qr = make_rsrc(Q + oq, bq), dOr = make_rsrc(dO + oq, bq);
+  const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
+  const rsrc_t L2r = make_rsrc(L2 + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const rsrc_t NDr = make_rsrc(ND + (size_t)bh * Nq, (uint32_t)Nq * 4);
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int kw0 = k0 + 32 * w;
+  const int krow = kw0 + l32;
+  const float c = exp2_coef(scale);
+
+  bf16x8 kf[DS], vf[DS];
+  load_kv_rows<D>(kf, vf, Kr, Vr, krow, g, neg);
+  // This wave's K rows (unnegated; rows past Nk read as zeros), the B operand of dS K.
+  B::MTile::template load<1>(Kr, kw0, ktile[w], 0, lane);
+  f32x16 dvt[DB], dkt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dvt[db] = zero16();
+    dkt[db] = zero16();
+  }
+  const int nmt = (Nq + 31) / 32;
+  const int lo = CAUSAL ? min(k0 / 32, nmt) : 0, hi = nmt;
+  if (lo < hi) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, lo * 32, smem, w, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int mt = lo; mt < hi; ++mt) {
+    bf16* buf = smem + ((mt - lo) & 1) * B::KV_BUF;
+    bf16* nbuf = smem + (((mt - lo) & 1) ^ 1) * B::KV_BUF;
+    const int m0 = mt * 32;
+    const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
+    KvOps<D> op;  // unused: transposed operands are read late (see KvOps)
+    if (mt + 1 < hi) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, m0 + 32, nbuf, w, lane);
+    if (active) {
+      kv_step<D, false, true>(buf, op, kf, vf, dvt, dkt, c, CAUSAL && m0 < kw0 + 31,
+                              krow - m0 - 4 * g, lane, l32, g, dstile[w]);
+      // dQ share of this wave's keys: register r of block db holds query 8(r/4) + 4g + r%4
+      // of the tile and column 32 db + l32 (at d = 16 the upper half of the block is padding).
+      f32x16 dq[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq[db] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = DTile::tfrag(dstile[w], 0, 16 * ks, lane);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dq[db] = mfma32(a, B::MTile::tfrag(ktile[w], 32 * db, 16 * ks, lane), dq[db]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = 32 * db + l32;
+        if (col < D)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[w][(8 * (r >> 2) + 4 * g + (r & 3)) * D + col] = dq[db][r];
+      }
+    }
+    // The four shares are summed in LDS and each wave adds 8 of the tile's rows (8 d
+    // consecutive floats of the accumulator) to it: one atomic addition per element and tile
+    // instead of four. Element e = 64 i + lane of the wave's block is row 8w + e/d, column
+    // e%d, so each atomic instruction covers 64 consecutive floats.
+    __syncthreads();
+    {
+      constexpr int NI = D / 8;  // atomic instructions per lane
+      float acc[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kv0 = k0 + 32 * v;
+        if (kv0 < Nk && (!CAUSAL || m0 + 31 >= kv0))
+#pragma unroll
+          for (int i = 0; i < NI; ++i) acc[i] += red[v][8 * w * D + 64 * i + lane];
+      }
+      float* dst = dqacc + oq + (size_t)(m0 + 8 * w) * D;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int e = 64 * i + lane;
+        if (m0 + 8 * w + e / D < Nq) unsafeAtomicAdd(dst + e, acc[i]);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (krow < Nk) {
+    store_rows_from_acc<D>(dK + ok + (size_t)krow * D, dkt, scale, g);
+    store_rows_from_acc<D>(dV + ok + (size_t)krow * D, dvt, 1.f, g);
+  }
+}
+
+// Zeroes n floats (the atomic dQ accumulator, which follows the per-row terms and so may be
+// only 4-byte aligned).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// dQ = bf16(scale * acc) elementwise (round to nearest even).
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
+                                                         bf16* __restrict__ dQ, long long n,
+                                                         float scale) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dQ[i] = (bf16)(acc[i] * scale);
 }
 
 // Runs step(n, cur) for n = first .. last-1 over tiles that fetch(n, dst) loads straight into
@@ -1677,6 +1816,60 @@ hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, co
       return hipErrorInvalidValue;
   }
 #undef FA_BWD
+}
+
+
+namespace {
+template <int D, bool CAUSAL>
+hipError_t bwd_atomic_t(const Shape& s, const void* Q, const void* K, const void* V,
+                        const void* dO, void* dQ, void* dK, void* dV, float* ws,
+                        hipStream_t stream) {
+  const long long rows = (long long)s.BH * s.Nq;
+  const float* L2 = ws;
+  const float* ND = ws + rows;
+  float* acc = ws + 2 * rows;
+  const long long n = rows * D;  // 0 when there are no query rows (dK = dV = 0 then)
+  if (n > 0) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, acc, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long grid = (long long)((s.Nk + 127) / 128) * s.BH;
+  if (grid > 0) {
+    hipLaunchKernelGGL((bwd_atomic_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
+                       (const bf16*)dO, acc, (bf16*)dK, (bf16*)dV, s.Nq, s.Nk, s.scale,
+                       s.scale < 0.f ? 1 : 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n > 0)
+    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, (const float*)acc, (bf16*)dQ, n, s.scale);
+  return hipGetLastError();
+}
+}  // namespace
+
+size_t bwd_atomic_workspace_bytes_bf16(const Shape& s) {
+  return (size_t)s.BH * (size_t)s.Nq * (2 + (size_t)s.d) * sizeof(float);
+}
+
+hipError_t launch_bwd_atomic_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                                  const void* dO, void* dQ, void* dK, void* dV, float* ws,
+                                  hipStream_t stream) {
+#define FA_ATOMIC_CASE(DD)                                                                 \
+  case DD:                                                                                 \
+    return s.causal ? bwd_atomic_t<DD, true>(s, Q, K, V, dO, dQ, dK, dV, ws, stream)       \
+                    : bwd_atomic_t<DD, false>(s, Q, K, V, dO, dQ, dK, dV, ws, stream);
+  switch (s.d) {
+    FA_ATOMIC_CASE(16)
+    FA_ATOMIC_CASE(32)
+    FA_ATOMIC_CASE(64)
+    FA_ATOMIC_CASE(128)
+  }
+#undef FA_ATOMIC_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

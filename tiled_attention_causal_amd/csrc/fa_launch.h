@@ -36,6 +36,13 @@ hipError_t launch_bwd_main_bf16(const Shape& s, const void* Q, const void* K, co
                                 const void* dO, void* dQ, void* dK, void* dV,
                                 const float* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+// The nondeterministic bf16 backward main step: dQ accumulated with fp32 atomics in the
+// workspace after the per-row terms (bwd_atomic_workspace_bytes_bf16 bytes in all), then
+// scaled and rounded into dQ. Three launches: zero, main, convert.
+size_t bwd_atomic_workspace_bytes_bf16(const Shape& s);
+hipError_t launch_bwd_atomic_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                                  const void* dO, void* dQ, void* dK, void* dV, float* workspace,
+                                  hipStream_t stream);
 // fp32: small grids likewise spread each workgroup's key (forward) or step (backward) range
 // over several workgroups when the workspace holds fwd_workspace_bytes_f32 or
 // bwd_split_workspace_bytes_f32 bytes; otherwise they run unsplit (fp32 needs no workspace).

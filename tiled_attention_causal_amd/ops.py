@@ -184,6 +184,39 @@ def backward_workspace_bytes(q: torch.Tensor, k: torch.Tensor) -> int:
     return _lib.load().fa_backward_workspace_bytes(_DTYPES[q.dtype], B, H, Nq, k.shape[2], d)
 
 
+def backward_atomic_workspace_bytes(q: torch.Tensor, k: torch.Tensor) -> int:
+    """Bytes of workspace fa_backward_atomic needs for these query and key tensors."""
+    B, H, Nq, d = q.shape
+    return _lib.load().fa_backward_atomic_workspace_bytes(_DTYPES[q.dtype], B, H, Nq,
+                                                          k.shape[2], d)
+
+
+def fa_backward_atomic(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                       lse: torch.Tensor, do: torch.Tensor, is_causal: bool = False,
+                       scale: float | None = None, dq: torch.Tensor | None = None,
+                       dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """fa_backward with dQ accumulated by fp32 atomic additions (bf16 only). dK and dV are
+    deterministic; dQ may differ between runs in its last bits (the order of the additions
+    varies). `workspace`, if given, must hold backward_atomic_workspace_bytes() bytes."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("fa_backward_atomic supports bf16 inputs only")
+    need = backward_atomic_workspace_bytes(q, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.nbytes < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    lib, (B, H, Nq, Nk, d), dq, dk, dv, ws, ws_bytes = _backward_args(
+        q, k, v, o, lse, do, dq, dk, dv, workspace)
+    sc = default_scale(d) if scale is None else float(scale)
+    st = lib.fa_backward_atomic(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
+                                v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                int(bool(is_causal)), sc, dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), ws.data_ptr(), ws_bytes, _stream_ptr(q))
+    _raise(st, "fa_backward_atomic")
+    return dq, dk, dv
+
+
 class FlashAttention(torch.autograd.Function):
     """Autograd wrapper: apply(Q, K, V, is_causal=False, scale=None) -> O."""
 
