@@ -1228,7 +1228,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_atomic_kernel(
         const int col = 32 * db + l32;
         if (col < D)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) red[w][(8 * (r >> 2) + 4 * g + (r & 3)) * D + col] = dq[db][r];
+          for (int r = 0; r < 16; ++r)
+            red[w][(8 * (r >> 2) + 4 * g + (r & 3)) * D + col] = dq[db][r];
       }
     }
     // The four shares are summed in LDS and each wave adds 8 of the tile's rows (8 d
