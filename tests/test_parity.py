@@ -607,3 +607,35 @@ def test_atomic_backward_empty_queries(gpu):
     fa_backward_atomic(q, k, v, o, lse, do, False, 0.125, dk=dk, dv=dv)
     torch.cuda.synchronize(gpu)
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_atomic_backward_dk_dv_deterministic(gpu):
+    """Only dQ goes through the atomics: dK and dV of two calls are bitwise equal."""
+    from tiled_attention_causal_amd import fa_backward_atomic, fa_forward
+    note("atomic backward determinism of dK, dV")
+    inp = make_inputs(2, 3, 640, 640, 64, "bf16", index=9990)
+    q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, True, 0.125)
+    a = fa_backward_atomic(q, k, v, o, lse, do, True, 0.125)
+    b = fa_backward_atomic(q, k, v, o, lse, do, True, 0.125)
+    torch.cuda.synchronize(gpu)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert torch.allclose(a[0].float(), b[0].float(), atol=2e-3, rtol=2 ** -7)
+
+
+def test_atomic_backward_agrees_with_two_pass_on_gpt_small(gpu):
+    """The GPT-small workload (4 x 12 heads of 1024, d = 64, causal), where the two-pass
+    backward takes the paired kernel at three workgroups per CU's worth of tiles."""
+    from tiled_attention_causal_amd import fa_backward, fa_backward_atomic, fa_forward
+    w = WORKLOADS["gpt_small"]
+    note(f"atomic vs two-pass on {w}")
+    inp = workload_inputs(w)
+    q, k, v, do = (inp[n].to(gpu) for n in ("q", "k", "v", "do"))
+    o, lse = fa_forward(q, k, v, True, w.scale)
+    ref = fa_backward(q, k, v, o, lse, do, True, w.scale)
+    got = fa_backward_atomic(q, k, v, o, lse, do, True, w.scale)
+    torch.cuda.synchronize(gpu)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        a, b = a.float(), b.float()
+        err = (a - b).abs()
+        assert torch.all(err <= 2 ** -7 * b.abs() + 2e-3), (name, float(err.max()))
