@@ -1174,14 +1174,16 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_atomic_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 dstile[4][DTile::ELEMS];  // a wave's dS^T
   __shared__ __attribute__((aligned(16))) float red[4][32 * D];  // the waves' dQ shares
   const int nkv = (Nk + 127) / 128;
-  const int bh = blockIdx.x / nkv, k0 = (blockIdx.x % nkv) * 128;
+  // A head's workgroups on one XCD where the grid allows (they add into the same rows).
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nkv, k0 = (lid % nkv) * 128;
   const size_t oq = (size_t)bh * Nq * D, ok = (size_t)bh * Nk * D;
   const uint32_t bq = (uint32_t)Nq * D * 2, bk = (uint32_t)Nk * D * 2;
   const rsrc_t Qr = make_rsrc(Q + oq, bq), dOr = make_rsrc(dO + oq, bq);
   const rsrc_t Kr = make_rsrc(K + ok, bk), Vr = make_rsrc(V + ok, bk);
   const rsrc_t L2r = make_rsrc(L2 + (size_t)bh * Nq, (uint32_t)Nq * 4);
   const rsrc_t NDr = make_rsrc(ND + (size_t)bh * Nq, (uint32_t)Nq * 4);
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int kw0 = k0 + 32 * w;
   const int krow = kw0 + l32;
   const float c = exp2_coef(scale);
