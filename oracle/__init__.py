@@ -4,6 +4,6 @@ from .attention import (  # noqa: F401
     forward,
     head_backward,
     head_forward,
-    head_sampled,
+    head_blocked,
     visible,
 )

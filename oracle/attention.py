@@ -35,10 +35,12 @@ Readings of points the pages leave open (each is also listed in the design notes
   * Causal alignment with Nq != Nk is top-left: visible iff j <= i, indices from 0.
   * scale is an argument; the callers pass float32(1/sqrt(d)), upcast exactly.
 
-Sampled evaluation (``head_sampled``) computes O, L, dQ for chosen query rows and dK, dV for
-chosen key rows of one head, with every sum complete; it needs L and D for every query row,
-which it takes from the full forward evaluated one block of whole rows at a time, and it
-uses D_i = sum_k dO_ik O_ik (equal to sum_j P_ij dP_ij; the pins check this identity).
+Row-block evaluation (``head_blocked``) computes every output of one head with the query
+rows taken a block of whole rows at a time, so that only one block's scores exist at once
+(for the long-context workload, whose full N x N score matrix would not fit comfortably).
+Each row's softmax is still over all of its visible keys, so this is the same definition,
+not an online softmax; dK and dV add up the blocks' contributions, and D is the same
+sum_j P_ij dP_ij as in head_backward.
 """
 from __future__ import annotations
 
@@ -50,7 +52,7 @@ __all__ = [
     "head_backward",
     "forward",
     "backward",
-    "head_sampled",
+    "head_blocked",
 ]
 
 
@@ -127,47 +129,48 @@ def backward(q, k, v, do, is_causal: bool, scale: float):
     return dq, dk, dv, dsum
 
 
-def head_sampled(q, k, v, do, is_causal: bool, scale: float, q_rows, k_rows,
-                 row_block: int = 1024):
-    """One head, selected outputs only, every sum complete.
+def head_blocked(q, k, v, do, is_causal: bool, scale: float, row_block: int = 1024,
+                 grads: bool = True):
+    """One head, every output, a block of whole query rows at a time.
 
-    Returns a dict with O and L and dQ at ``q_rows`` and dK and dV at ``k_rows``.
+    q and do are [Nq, d], k and v [Nk, d]. Returns (O, L, dQ, dK, dV, D); with
+    grads=False only O and L are formed and the rest are None.
+
+    Same definitions as head_forward and head_backward. Under causal masking the rows
+    [r0, r1) of a block see no key at or past r1, so their scores are formed against keys
+    [0, min(Nk, r1)) only: every other key's P is exactly 0 and adds nothing to any sum.
     """
-    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    q, k, v = _f64(q), _f64(k), _f64(v)
     nq, nk = q.shape[0], k.shape[0]
     sc = np.float64(scale)
-    q_rows = np.asarray(q_rows, dtype=np.int64)
-    k_rows = np.asarray(k_rows, dtype=np.int64)
-
-    # L and O for every query row, a block of whole rows at a time.
-    lse = np.empty(nq)
     o = np.empty((nq, v.shape[1]))
+    lse = np.empty(nq)
+    if grads:
+        do = _f64(do)
+        dq = np.empty_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        dsum = np.empty(nq)
     for r0 in range(0, nq, row_block):
         r1 = min(nq, r0 + row_block)
-        s = (q[r0:r1] @ k.T) * sc
+        kn = min(nk, r1) if is_causal else nk  # the keys any row of the block can see
+        s = (q[r0:r1] @ k[:kn].T) * sc
         if is_causal:
-            vis = np.arange(nk)[None, :] <= np.arange(r0, r1)[:, None]
+            vis = np.arange(kn)[None, :] <= np.arange(r0, r1)[:, None]
         else:
-            vis = np.ones((r1 - r0, nk), dtype=bool)
+            vis = np.ones((r1 - r0, kn), dtype=bool)
         p, lse[r0:r1] = _softmax_rows(s, vis)
-        o[r0:r1] = p @ v
-    dsum = np.sum(do * o, axis=-1)
-
-    # Query rows: dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j.
-    s = (q[q_rows] @ k.T) * sc
-    vis_q = np.arange(nk)[None, :] <= q_rows[:, None] if is_causal else np.ones(s.shape, bool)
-    p = np.where(vis_q, np.exp(np.where(vis_q, s, 0.0) - lse[q_rows][:, None]), 0.0)
-    dp = do[q_rows] @ v.T
-    ds = p * (dp - dsum[q_rows][:, None])
-    dq = sc * (ds @ k)
-
-    # Key rows: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i.
-    s = (q @ k[k_rows].T) * sc  # [nq, len(k_rows)]
-    vis_k = k_rows[None, :] <= np.arange(nq)[:, None] if is_causal else np.ones(s.shape, bool)
-    p = np.where(vis_k, np.exp(np.where(vis_k, s, 0.0) - lse[:, None]), 0.0)
-    dv = p.T @ do
-    dp = do @ v[k_rows].T
-    ds = p * (dp - dsum[:, None])
-    dk = sc * (ds.T @ q)
-    return {"O": o[q_rows], "L": lse[q_rows], "dQ": dq, "dK": dk, "dV": dv,
-            "D": dsum[q_rows]}
+        del s, vis
+        o[r0:r1] = p @ v[:kn]
+        if grads:
+            g = do[r0:r1]
+            dp = g @ v[:kn].T
+            dsum[r0:r1] = np.sum(p * dp, axis=-1)
+            ds = p * (dp - dsum[r0:r1, None])
+            del dp
+            dq[r0:r1] = sc * (ds @ k[:kn])
+            dk[:kn] += sc * (ds.T @ q[r0:r1])
+            dv[:kn] += p.T @ g
+    if not grads:
+        return o, lse, None, None, None, None
+    return o, lse, dq, dk, dv, dsum

@@ -220,19 +220,108 @@ def test_batched_matches_heads():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("nq,nk", [(40, 40), (37, 53), (53, 37)])
-def test_sampled_matches_full(causal, nq, nk):
+@pytest.mark.parametrize("nq,nk", [(40, 40), (37, 53), (53, 37), (1, 9), (9, 1)])
+@pytest.mark.parametrize("row_block", [1, 7, 16, 64])
+def test_blocked_matches_full(causal, nq, nk, row_block):
+    """The row-block form gives the whole-matrix form's outputs, for blocks that divide Nq,
+    leave a ragged last block, or exceed Nq."""
     q, k, v, g = rand((nq, 8), 60), rand((nk, 8), 61), rand((nk, 8), 62), rand((nq, 8), 63)
     o, lse, _ = oracle.head_forward(q, k, v, causal, 0.3)
-    dq, dk, dv, _ = oracle.head_backward(q, k, v, g, causal, 0.3)
-    qr = np.array([0, 1, nq // 2, nq - 1])
-    kr = np.array([0, nk // 3, nk - 1])
-    s = oracle.head_sampled(q, k, v, g, causal, 0.3, qr, kr, row_block=16)
-    np.testing.assert_allclose(s["O"], o[qr], rtol=0, atol=1e-13)
-    np.testing.assert_allclose(s["L"], lse[qr], rtol=0, atol=1e-13)
-    np.testing.assert_allclose(s["dQ"], dq[qr], rtol=0, atol=1e-12)
-    np.testing.assert_allclose(s["dK"], dk[kr], rtol=0, atol=1e-12)
-    np.testing.assert_allclose(s["dV"], dv[kr], rtol=0, atol=1e-12)
+    dq, dk, dv, dsum = oracle.head_backward(q, k, v, g, causal, 0.3)
+    got = oracle.head_blocked(q, k, v, g, causal, 0.3, row_block=row_block)
+    for name, a, b in zip(("O", "L", "dQ", "dK", "dV", "D"), got, (o, lse, dq, dk, dv, dsum)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12, err_msg=name)
+    o2, l2, *rest = oracle.head_blocked(q, k, v, None, causal, 0.3, row_block=row_block,
+                                        grads=False)
+    np.testing.assert_array_equal(o2, got[0])
+    np.testing.assert_array_equal(l2, got[1])
+    assert rest == [None] * 4
+
+
+def _blocked_pair(row_block, blocked=None):
+    """(fwd, bwd) with the signatures of head_forward / head_backward, computed by the
+    row-block form; fwd has no P to return."""
+    blocked = blocked or oracle.head_blocked
+
+    def fwd(q, k, v, causal, scale):
+        o, lse, *_ = blocked(q, k, v, None, causal, scale, row_block=row_block, grads=False)
+        return o, lse, None
+
+    def bwd(q, k, v, do, causal, scale):
+        _, _, dq, dk, dv, dsum = blocked(q, k, v, do, causal, scale, row_block=row_block)
+        return dq, dk, dv, dsum
+
+    return fwd, bwd
+
+
+# Every pin that reads only O, L and the gradients (the row-block form keeps no P).
+BLOCKED_PINS = [p for p in PINS if p not in (pin_rows_sum_to_one, pin_causal_zeros)]
+
+
+@pytest.mark.parametrize("row_block", [2, 3])
+@pytest.mark.parametrize("pin", BLOCKED_PINS, ids=lambda f: f.__name__)
+def test_blocked_oracle_pin(pin, row_block):
+    pin(*_blocked_pair(row_block))
+
+
+def _mut_blocked(kind):
+    """head_blocked with one planted mistake in its blocking."""
+    def blocked(q, k, v, do, causal, scale, row_block=1024, grads=True):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        nq, nk = q.shape[0], k.shape[0]
+        o, lse = np.empty((nq, v.shape[1])), np.empty(nq)
+        if grads:
+            do = np.asarray(do, np.float64)
+            dq, dk, dv, dsum = np.empty_like(q), np.zeros_like(k), np.zeros_like(v), np.empty(nq)
+        for r0 in range(0, nq, row_block):
+            r1 = min(nq, r0 + row_block)
+            kn = min(nk, r1) if causal else nk
+            if kind == "keys_short" and causal and kn > 1:
+                kn -= 1
+            s = (q[r0:r1] @ k[:kn].T) * scale
+            rows = np.arange(r0, r1) + (1 if kind == "rows_shifted" else 0)
+            vis = (np.arange(kn)[None, :] <= rows[:, None]) if causal else np.ones(s.shape, bool)
+            p, lse[r0:r1] = oa._softmax_rows(s, vis)
+            o[r0:r1] = p @ v[:kn]
+            if grads:
+                g = do[r0:r1]
+                dp = g @ v[:kn].T
+                dsum[r0:r1] = np.sum(p * dp, axis=-1)
+                ds = p * (dp - dsum[r0:r1, None])
+                dq[r0:r1] = scale * (ds @ k[:kn])
+                if kind == "dk_overwritten":
+                    dk[:kn] = scale * (ds.T @ q[r0:r1])
+                else:
+                    dk[:kn] += scale * (ds.T @ q[r0:r1])
+                if kind == "dv_first_block_only":
+                    if r0 == 0:
+                        dv[:kn] += p.T @ g
+                else:
+                    dv[:kn] += p.T @ g
+        if not grads:
+            return o, lse, None, None, None, None
+        return o, lse, dq, dk, dv, dsum
+    return blocked
+
+
+@pytest.mark.parametrize("kind", ["keys_short", "rows_shifted", "dk_overwritten",
+                                  "dv_first_block_only"])
+def test_blocked_pins_catch_planted_mistake(kind):
+    fwd, bwd = _blocked_pair(3, _mut_blocked(kind))
+    caught = []
+    for pin in BLOCKED_PINS:
+        try:
+            pin(fwd, bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted blocking mistake {kind}"
+
+
+def test_blocked_mutant_harness_without_mistake_passes():
+    """The copy the mistakes are planted in passes every pin when no mistake is planted."""
+    fwd, bwd = _blocked_pair(3, _mut_blocked("none"))
+    for pin in BLOCKED_PINS:
+        pin(fwd, bwd)
 
 
 def test_minus_1e6_mask_reading():
