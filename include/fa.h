@@ -26,7 +26,7 @@
  * inputs.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its kernels on
- * `stream` (a hipStream_t; NULL means the default stream) and returns. Results are ready
+ * `stream` (NULL means the default stream) and returns. Results are ready
  * once the stream has been synchronised. A fault inside a kernel surfaces at that
  * synchronisation, as for any HIP kernel.
  *
@@ -56,6 +56,10 @@
 extern "C" {
 #endif
 
+/* The HIP runtime's stream handle (the same typedef as <hip/hip_runtime_api.h>, so either
+ * header may come first). NULL is the default stream. */
+typedef struct ihipStream_t* hipStream_t;
+
 #if defined(__GNUC__) || defined(__clang__)
 #define FA_API __attribute__((visibility("default")))
 #else
@@ -75,19 +79,6 @@ typedef enum fa_dtype {
 } fa_dtype;
 
 /*
- * fa_forward_workspace_bytes -- bytes of device workspace fa_forward can use for these
- * arguments (0 when it needs none, and for arguments fa_forward would reject).
- *
- * Small causal bf16 grids (Nq = Nk a multiple of 128, any d, few tiles per head)
- * spread each pair of query tiles over several workgroups so that every CU has work; their
- * partial softmax states go to the workspace and a second launch merges them (the same
- * rescale the online softmax applies between key tiles, problem flash_forward). The size is
- * (Nq/128) * B * H * ways * 2 * (16*ceil(d/32) + 2) * 128 * 4 bytes, with ways in {2, 4, 8}.
- */
-FA_API size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
-                                         int64_t Nk, int64_t d, int is_causal);
-
-/*
  * fa_forward -- O = softmax(Q K^T * scale [+ causal mask]) V and L = row logsumexp.
  *
  * Follows problem flash_forward: the kernel walks key tiles with an online softmax
@@ -105,16 +96,46 @@ FA_API size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, i
  *   scale        multiplies Q K^T (finite; usually 1/sqrt(d))
  *   O            [B,H,Nq,d] dtype, written
  *   L            [B,H,Nq] float32, written (natural-log logsumexp of the scaled scores)
- *   workspace    device scratch, caller-owned, 16-byte aligned; may be NULL with
- *                workspace_bytes = 0. With fewer than fa_forward_workspace_bytes bytes the
- *                call still succeeds: small causal grids then run one workgroup per pair of
- *                query tiles (slower, same results up to the order of the final merge).
- *                The call overwrites it; concurrent calls must not share one.
  *   stream       hipStream_t or NULL
+ *
+ * Needs no workspace. Small causal grids, which could use one to spread their work over
+ * more of the GPU, run one workgroup per pair of query tiles here; fa_forward_with_workspace
+ * is the same call with that workspace.
  */
-FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                     const void* Q, const void* K, const void* V, int is_causal, float scale,
-                     void* O, float* L, void* workspace, size_t workspace_bytes, void* stream);
+FA_API fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                            int64_t d, const void* Q, const void* K, const void* V,
+                            int is_causal, float scale, void* O, float* L, hipStream_t stream);
+
+/*
+ * fa_forward_workspace_bytes -- bytes of device workspace fa_forward_with_workspace can use
+ * for these arguments (0 when it needs none, and for arguments it would reject).
+ *
+ * Small causal bf16 grids (Nq = Nk a multiple of 128, any d, few tiles per head)
+ * spread each pair of query tiles over several workgroups so that every CU has work; their
+ * partial softmax states go to the workspace and a second launch merges them (the same
+ * rescale the online softmax applies between key tiles, problem flash_forward). The size is
+ * (Nq/128) * B * H * ways * 2 * (16*ceil(d/32) + 2) * 128 * 4 bytes, with ways in {2, 4, 8}.
+ * fp32 grids of few query tiles spread each tile's keys likewise.
+ */
+FA_API size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                         int64_t Nk, int64_t d, int is_causal);
+
+/*
+ * fa_forward_with_workspace -- fa_forward with a caller-owned device workspace.
+ *
+ *   workspace    device scratch, 16-byte aligned; may be NULL with workspace_bytes = 0.
+ *                With fa_forward_workspace_bytes() bytes, small grids spread their work
+ *                over more workgroups; with fewer the call still succeeds and runs as
+ *                fa_forward does (same results up to the order of the final merge). The
+ *                call overwrites it; concurrent calls must not share one.
+ * Every other argument, and the errors, as for fa_forward; in addition a workspace that is
+ * NULL or not 16-byte aligned while workspace_bytes > 0 is FA_ERROR_INVALID_VALUE.
+ */
+FA_API fa_status fa_forward_with_workspace(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                           int64_t Nk, int64_t d, const void* Q, const void* K,
+                                           const void* V, int is_causal, float scale, void* O,
+                                           float* L, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
 
 /*
  * fa_backward_workspace_bytes -- bytes of device workspace fa_backward can use for these
@@ -159,7 +180,7 @@ FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, i
                       const void* Q, const void* K, const void* V, const void* O,
                       const float* L, const void* dO, int is_causal, float scale,
                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      hipStream_t stream);
 
 /*
  * fa_backward_preprocess -- the backward's preprocessing step on its own: for every query
@@ -172,7 +193,7 @@ FA_API fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, i
  */
 FA_API fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
                                  int64_t d, const void* O, const float* L, const void* dO,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_backward_main -- everything fa_backward does after fa_backward_preprocess: dQ, dK and
@@ -185,7 +206,7 @@ FA_API fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t 
                            int64_t d, const void* Q, const void* K, const void* V,
                            const void* O, const float* L, const void* dO, int is_causal,
                            float scale, void* dQ, void* dK, void* dV, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_backward_atomic_workspace_bytes -- bytes of device workspace fa_backward_atomic needs
@@ -214,7 +235,23 @@ FA_API fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_
                                     const void* V, const void* O, const float* L,
                                     const void* dO, int is_causal, float scale, void* dQ,
                                     void* dK, void* dV, void* workspace,
-                                    size_t workspace_bytes, void* stream);
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_forward_kernel_name, fa_backward_kernel_name -- the name, as a profiler lists it, of the
+ * attention kernel that fa_forward_with_workspace (fa_forward: workspace_bytes = 0) or
+ * fa_backward / fa_backward_main with `workspace_bytes` of workspace launch for these
+ * arguments, for example "fwd_causal_split_kernel<64>" (the library's choice of kernel
+ * depends on the grid's size and shape, and on the workspace). The launchers take the same
+ * decision from the same code. Static storage, never NULL; "" for arguments the calls would
+ * reject.
+ */
+FA_API const char* fa_forward_kernel_name(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                          int64_t Nk, int64_t d, int is_causal,
+                                          size_t workspace_bytes);
+FA_API const char* fa_backward_kernel_name(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                           int64_t Nk, int64_t d, int is_causal,
+                                           size_t workspace_bytes);
 
 /* fa_status_string -- static, NUL-terminated name of a status code (never NULL). */
 FA_API const char* fa_status_string(fa_status status);

@@ -29,9 +29,62 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == ["fa_backward", "fa_backward_atomic",
-                                  "fa_backward_atomic_workspace_bytes", "fa_backward_main",
+                                  "fa_backward_atomic_workspace_bytes",
+                                  "fa_backward_kernel_name", "fa_backward_main",
                                   "fa_backward_preprocess", "fa_backward_workspace_bytes",
-                                  "fa_forward", "fa_forward_workspace_bytes", "fa_status_string"]
+                                  "fa_forward", "fa_forward_kernel_name",
+                                  "fa_forward_with_workspace", "fa_forward_workspace_bytes",
+                                  "fa_status_string"]
+
+
+def _prototype(name):
+    """(return type, [(parameter type, name), ...]) of `name` as include/fa.h declares it,
+    whitespace normalised."""
+    text = open(HEADER).read()
+    m = re.search(r"FA_API\s+([\w\s\*]+?)\s*\b" + name + r"\s*\(([^)]*)\)", text)
+    assert m, name
+    params = []
+    for a in m.group(2).split(","):
+        a = " ".join(a.split())
+        t, n = re.match(r"(.*?)\s*\b(\w+)$", a).groups()
+        params.append((t.replace(" *", "*"), n))
+    return " ".join(m.group(1).split()), params
+
+
+# The boundary's contract: the entry points, argument lists and types of the scope table
+# (problems flash_forward / flash_backward: forward(Q, K, V, is_causal) -> O with L saved;
+# the backward takes the forward's mask and scale with O, L and dO).
+CONTRACT = {
+    "fa_forward": ("fa_status", [
+        ("fa_dtype", "dtype"), ("int64_t", "B"), ("int64_t", "H"), ("int64_t", "Nq"),
+        ("int64_t", "Nk"), ("int64_t", "d"), ("const void*", "Q"), ("const void*", "K"),
+        ("const void*", "V"), ("int", "is_causal"), ("float", "scale"), ("void*", "O"),
+        ("float*", "L"), ("hipStream_t", "stream")]),
+    "fa_backward_workspace_bytes": ("size_t", [
+        ("fa_dtype", "dtype"), ("int64_t", "B"), ("int64_t", "H"), ("int64_t", "Nq"),
+        ("int64_t", "Nk"), ("int64_t", "d")]),
+    "fa_backward": ("fa_status", [
+        ("fa_dtype", "dtype"), ("int64_t", "B"), ("int64_t", "H"), ("int64_t", "Nq"),
+        ("int64_t", "Nk"), ("int64_t", "d"), ("const void*", "Q"), ("const void*", "K"),
+        ("const void*", "V"), ("const void*", "O"), ("const float*", "L"),
+        ("const void*", "dO"), ("int", "is_causal"), ("float", "scale"), ("void*", "dQ"),
+        ("void*", "dK"), ("void*", "dV"), ("void*", "workspace"), ("size_t", "workspace_bytes"),
+        ("hipStream_t", "stream")]),
+    "fa_status_string": ("const char*", [("fa_status", "status")]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONTRACT))
+def test_header_matches_the_contract_signatures(name):
+    assert _prototype(name) == CONTRACT[name]
+
+
+def test_status_and_dtype_codes_match_the_contract():
+    text = open(HEADER).read()
+    for sym, val in (("FA_SUCCESS", 0), ("FA_ERROR_INVALID_VALUE", 1),
+                     ("FA_ERROR_NOT_SUPPORTED", 2), ("FA_ERROR_LAUNCH_FAILED", 3),
+                     ("FA_DTYPE_F32", 0), ("FA_DTYPE_BF16", 1)):
+        assert re.search(r"\b" + sym + r"\s*=\s*" + str(val) + r"\b", text), sym
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -111,8 +164,14 @@ BAD = 0x10002  # misaligned
 
 def fwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, causal=1, scale=0.125,
         o=P, lse=P, ws=None, ws_bytes=0):
-    return lib.fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o, lse, ws, ws_bytes,
-                          None)
+    """fa_forward_with_workspace, and fa_forward (the same validation) when there is no
+    workspace: both must agree."""
+    code = lib.fa_forward_with_workspace(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o,
+                                         lse, ws, ws_bytes, None)
+    if ws is None and ws_bytes == 0:
+        assert lib.fa_forward(dtype, B, H, Nq, Nk, d, q, k, v, causal, scale, o, lse,
+                              None) == code
+    return code
 
 
 def bwd(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
@@ -245,3 +304,29 @@ def test_backward_atomic_empty_is_a_noop(lib):
     assert bwd_atomic(lib, B=0) == 0
     assert bwd_atomic(lib, Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None,
                       dq=None, dk=None, dv=None) == 0
+
+
+def test_kernel_names_follow_dispatch(lib):
+    """The library names the kernels its dispatch picks (the launchers and the name queries
+    share one plan per pass)."""
+    def names(dtype, B, H, Nq, Nk, d, causal, fws=0, bws=1 << 40):
+        return (lib.fa_forward_kernel_name(dtype, B, H, Nq, Nk, d, causal, fws).decode(),
+                lib.fa_backward_kernel_name(dtype, B, H, Nq, Nk, d, causal, bws).decode())
+    # 8 heads of 4096 at d = 64, causal: 256 tile pairs fill the CUs once
+    assert names(1, 8, 1, 4096, 4096, 64, 1) == ("fwd_causal_split_kernel<64>",
+                                                 "bwd_causal_paired_kernel<64>")
+    assert names(1, 4, 12, 1024, 1024, 64, 1) == ("fwd_causal_paired_kernel<64>",
+                                                  "bwd_causal_paired_kernel<64>")
+    assert names(1, 4, 25, 2048, 2048, 64, 1) == ("fwd_kernel<64, true>", "bwd_kernel<64, true>")
+    assert names(1, 4, 25, 2048, 2048, 64, 0) == ("fwd_kernel<64, false>",
+                                                  "bwd_kernel<64, false>")
+    assert names(1, 8, 1, 16384, 16384, 128, 1) == ("fwd_kernel<128, true>",
+                                                    "bwd_kernel<128, true>")
+    assert names(1, 1, 2, 2048, 2048, 128, 1) == ("fwd_causal_paired_kernel<128>",
+                                                  "bwd_kernel<128, true>")
+    assert names(1, 1, 1, 512, 512, 16, 1) == ("fwd_causal_split_kernel<16>",
+                                               "bwd_kernel<16, true>")
+    assert names(1, 1, 1, 200, 300, 64, 1) == ("fwd_kernel<64, true>", "bwd_kernel<64, true>")
+    assert names(0, 1, 1, 128, 128, 16, 1) == ("fwd_f32_kernel<16, true>",
+                                               "bwd_f32_kernel<16, true>")
+    assert names(1, 1, 1, 128, 128, 48, 1) == ("", "")     # rejected arguments

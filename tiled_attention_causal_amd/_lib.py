@@ -26,8 +26,10 @@ SIGNATURES = {
     "fa_forward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                                      ctypes.c_int]),
     "fa_forward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
-                                  ctypes.c_int, ctypes.c_float, _ptr, _ptr, _ptr,
-                                  ctypes.c_size_t, _ptr]),
+                                  ctypes.c_int, ctypes.c_float, _ptr, _ptr, _ptr]),
+    "fa_forward_with_workspace": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                 _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float,
+                                                 _ptr, _ptr, _ptr, ctypes.c_size_t, _ptr]),
     "fa_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64]),
     "fa_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                    _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float, _ptr, _ptr,
@@ -42,6 +44,10 @@ SIGNATURES = {
     "fa_backward_main": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr,
                                         _ptr, _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float,
                                         _ptr, _ptr, _ptr, _ptr, ctypes.c_size_t, _ptr]),
+    "fa_forward_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                 ctypes.c_int, ctypes.c_size_t]),
+    "fa_backward_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_int, ctypes.c_size_t]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 

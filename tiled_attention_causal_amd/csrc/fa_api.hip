@@ -86,9 +86,10 @@ size_t fa_forward_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t 
                                 : fa::fwd_workspace_bytes_f32(s);
 }
 
-fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                     const void* Q, const void* K, const void* V, int is_causal, float scale,
-                     void* O, float* L, void* workspace, size_t workspace_bytes, void* stream) {
+fa_status fa_forward_with_workspace(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                    int64_t d, const void* Q, const void* K, const void* V,
+                                    int is_causal, float scale, void* O, float* L,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   fa::Shape s;
   const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, &s);
   if (st != FA_SUCCESS) return st;
@@ -100,7 +101,7 @@ fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
   if (bad_ptr(Q) || bad_ptr(K) || bad_ptr(V) || bad_ptr(O) || L == nullptr ||
       (reinterpret_cast<uintptr_t>(L) & 3u) != 0)
     return FA_ERROR_INVALID_VALUE;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipStream_t hs = stream;
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
     e = fa::launch_fwd_bf16(s, Q, K, V, O, L, static_cast<float*>(workspace), workspace_bytes,
@@ -110,6 +111,31 @@ fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
                            static_cast<const float*>(V), static_cast<float*>(O), L,
                            static_cast<float*>(workspace), workspace_bytes, hs);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
+}
+
+fa_status fa_forward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     const void* Q, const void* K, const void* V, int is_causal, float scale,
+                     void* O, float* L, hipStream_t stream) {
+  return fa_forward_with_workspace(dtype, B, H, Nq, Nk, d, Q, K, V, is_causal, scale, O, L,
+                                   nullptr, 0, stream);
+}
+
+const char* fa_forward_kernel_name(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                   int64_t Nk, int64_t d, int is_causal,
+                                   size_t workspace_bytes) {
+  fa::Shape s;
+  if (check_common(dtype, B, H, Nq, Nk, d, 1.f, is_causal, &s) != FA_SUCCESS) return "";
+  return dtype == FA_DTYPE_BF16 ? fa::fwd_kernel_name_bf16(s, workspace_bytes)
+                                : fa::fwd_kernel_name_f32(s);
+}
+
+const char* fa_backward_kernel_name(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                    int64_t Nk, int64_t d, int is_causal,
+                                    size_t workspace_bytes) {
+  fa::Shape s;
+  if (check_common(dtype, B, H, Nq, Nk, d, 1.f, is_causal, &s) != FA_SUCCESS) return "";
+  return dtype == FA_DTYPE_BF16 ? fa::bwd_kernel_name_bf16(s, workspace_bytes)
+                                : fa::bwd_kernel_name_f32(s);
 }
 
 // Validation shared by fa_backward and fa_backward_main (which read the same arguments).
@@ -138,7 +164,7 @@ static fa_status check_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq
 
 fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t d,
                                  const void* O, const float* L, const void* dO,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   fa::Shape s;
   // Keys play no part here; Nk = 0 keeps the size checks to the query side.
   const fa_status st = check_common(dtype, B, H, Nq, 0, d, 1.f, 0, &s);
@@ -150,7 +176,7 @@ fa_status fa_backward_preprocess(fa_dtype dtype, int64_t B, int64_t H, int64_t N
       bad_ptr(O) || bad_ptr(dO) || L == nullptr || (reinterpret_cast<uintptr_t>(L) & 3u) != 0)
     return FA_ERROR_INVALID_VALUE;
   const hipError_t e = fa::launch_bwd_prep_bf16(s, O, L, dO, static_cast<float*>(workspace),
-                                                static_cast<hipStream_t>(stream));
+                                                stream);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
 }
 
@@ -158,14 +184,14 @@ fa_status fa_backward_main(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
                            int64_t d, const void* Q, const void* K, const void* V,
                            const void* O, const float* L, const void* dO, int is_causal,
                            float scale, void* dQ, void* dK, void* dV, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, hipStream_t stream) {
   fa::Shape s;
   bool nothing = false;
   const fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal,
                                       scale, dQ, dK, dV, workspace, workspace_bytes, &s,
                                       &nothing);
   if (st != FA_SUCCESS || nothing) return st;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipStream_t hs = stream;
   hipError_t e;
   if (dtype == FA_DTYPE_BF16)
     e = fa::launch_bwd_main_bf16(s, Q, K, V, dO, dQ, dK, dV,
@@ -183,7 +209,7 @@ fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t 
                       const void* Q, const void* K, const void* V, const void* O,
                       const float* L, const void* dO, int is_causal, float scale, void* dQ,
                       void* dK, void* dV, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      hipStream_t stream) {
   fa::Shape s;
   bool nothing = false;
   fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale,
@@ -207,7 +233,7 @@ fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, i
                              int64_t d, const void* Q, const void* K, const void* V,
                              const void* O, const float* L, const void* dO, int is_causal,
                              float scale, void* dQ, void* dK, void* dV, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, hipStream_t stream) {
   fa::Shape s;
   bool nothing = false;
   fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale,
@@ -219,7 +245,7 @@ fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, i
   if (st != FA_SUCCESS) return st;
   const hipError_t e =
       fa::launch_bwd_atomic_bf16(s, Q, K, V, dO, dQ, dK, dV, static_cast<float*>(workspace),
-                                 static_cast<hipStream_t>(stream));
+                                 stream);
   return e == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILED;
 }
 

@@ -1654,44 +1654,58 @@ size_t bwd_split_workspace_bytes_bf16(const Shape& s) {
 
 namespace {
 
+// Which forward kernel a call runs, and the workgroups per tile pair (ns > 1: the split
+// launch whose partial results fwd_split_combine_kernel merges). Pairing pays off only when
+// one 128-query tile per workgroup leaves CUs idle or runs a single wave per SIMD anyway;
+// larger grids keep the plain kernel (shared K/V stream, two waves per SIMD). Up to one tile
+// pair per CU, d <= 64 takes the eight-wave split kernel and d = 128 the paired kernel; up
+// to two (d = 32, 64), the four-wave paired kernel (two fit a CU), whose balanced steps beat
+// the plain kernel's longest-tile tail.
+enum FwdKernel { kFwdPlain, kFwdPaired, kFwdSplit };
+struct FwdPlan {
+  FwdKernel kernel;
+  int ns;
+};
+
+FwdPlan fwd_plan(const Shape& s, size_t ws_bytes) {
+  const long long pairs = (long long)(s.Nq / 128) * s.BH;
+  const bool square = s.causal && s.Nq == s.Nk && s.Nq % 128 == 0;
+  if (square && s.d >= 32 && s.d <= 64 && pairs > kNumCUs && pairs <= 2 * kNumCUs)
+    return {kFwdPaired, 1};
+  if (square && pairs <= kNumCUs) {
+    int ns = fwd_split_ways(s);
+    if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
+    return {s.d <= 64 ? kFwdSplit : kFwdPaired, ns};
+  }
+  return {kFwdPlain, 1};
+}
+
 template <int D, bool CAUSAL>
 hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, void* O, float* L,
                  float* ws, size_t ws_bytes, hipStream_t stream) {
-  // Pairing pays off only when one 128-query tile per workgroup leaves CUs idle or runs a
-  // single wave per SIMD anyway; larger grids keep the plain kernel (shared K/V stream, two
-  // waves per SIMD). Up to one tile pair per CU, d <= 64 takes the eight-wave split kernel;
-  // up to two (d = 32, 64), the four-wave paired kernel (two fit a CU), whose balanced steps
-  // beat the plain kernel's longest-tile tail.
+  const FwdPlan pl = fwd_plan(s, ws_bytes);
+  const int neg = s.scale < 0.f ? 1 : 0;
   if constexpr (CAUSAL) {
-    const long long pairs = (long long)(s.Nq / 128) * s.BH;
-    if constexpr (D >= 32 && D <= 64) {
-      if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs > kNumCUs && pairs <= 2 * kNumCUs) {
-        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)pairs), dim3(256), 0,
-                           stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L,
-                           s.Nq, s.scale, s.scale < 0.f ? 1 : 0, 1, nullptr);
-        return hipGetLastError();
+    if (pl.kernel != kFwdPlain) {
+      const unsigned grid = (unsigned)((long long)(s.Nq / 128) * s.BH * pl.ns);
+      if (pl.kernel == kFwdSplit) {
+        if constexpr (D <= 64)
+          hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3(grid), dim3(512), 0, stream,
+                             (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L, s.Nq,
+                             s.scale, neg, pl.ns, ws);
+      } else {
+        if constexpr (D >= 32)
+          hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3(grid), dim3(256), 0, stream,
+                             (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L, s.Nq,
+                             s.scale, neg, pl.ns, ws);
       }
-    }
-    if (s.Nq == s.Nk && s.Nq % 128 == 0 && pairs <= kNumCUs) {
-      int ns = fwd_split_ways(s);
-      if (ns > 1 && ws_bytes < fwd_workspace_bytes_bf16(s)) ns = 1;
-      if constexpr (D <= 64)
-        hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3((unsigned)(pairs * ns)),
-                           dim3(512), 0, stream, (const bf16*)Q, (const bf16*)K,
-                           (const bf16*)V, (bf16*)O, L, s.Nq, s.scale, s.scale < 0.f ? 1 : 0,
-                           ns, ws);
-      else
-        hipLaunchKernelGGL((fwd_causal_paired_kernel<D>), dim3((unsigned)(pairs * ns)),
-                           dim3(256), 0, stream, (const bf16*)Q, (const bf16*)K,
-                           (const bf16*)V, (bf16*)O, L, s.Nq, s.scale, s.scale < 0.f ? 1 : 0,
-                           ns, ws);
-      if (ns > 1) {
+      if (pl.ns > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((fwd_split_combine_kernel<D>),
                            dim3((unsigned)((long long)s.BH * (s.Nq / 64))),
                            dim3(128 * ((D + 31) / 32)), 0, stream, (const float*)ws, (bf16*)O,
-                           L, s.Nq, s.scale, ns);
+                           L, s.Nq, s.scale, pl.ns);
       }
       return hipGetLastError();
     }
@@ -1700,7 +1714,7 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
   const long long grid = (long long)nqt * s.BH;
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, stream,
                      (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L, s.Nq, s.Nk,
-                     s.scale, s.scale < 0.f ? 1 : 0);
+                     s.scale, neg);
   return hipGetLastError();
 }
 
@@ -1717,6 +1731,28 @@ hipError_t bwd_prep_t(const Shape& s, const void* O, const float* L, const void*
   return hipGetLastError();
 }
 
+// Which backward main kernel a call runs, and the workgroups each workgroup's steps are
+// spread over (ns > 1: fp32 partial sums after the per-row terms in the workspace, added up
+// by bwd_split_combine_kernel). The paired kernel takes causal square grids of up to three
+// of its workgroups per CU at d = 32 and 64, where the plain grid (two 128-row tiles per
+// head per 128 rows) would leave the longest tile on the critical path (d = 128 grids at
+// this size are rare, and hipcc 7.2 cannot register-allocate that instantiation, so it is
+// not built).
+enum BwdKernel { kBwdPlain, kBwdPaired };
+struct BwdPlan {
+  BwdKernel kernel;
+  int ns;
+};
+
+BwdPlan bwd_plan(const Shape& s, size_t ws_bytes, bool ws_aligned16) {
+  const long long rows = (long long)s.BH * s.Nq;
+  int ns = bwd_split_ways(s);
+  const size_t split_bytes = (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
+  if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes || !ws_aligned16))
+    ns = 1;  // the partial tiles are written and read 16 bytes at a time
+  return {bwd_uses_paired(s) ? kBwdPaired : kBwdPlain, ns};
+}
+
 template <int D, bool CAUSAL>
 hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                  void* dQ, void* dK, void* dV, const float* ws, size_t ws_bytes,
@@ -1724,23 +1760,15 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   const long long rows = (long long)s.BH * s.Nq;
   const float* L2 = ws;
   const float* ND = ws + rows;
-  // Partial sums of split grids follow the two per-row arrays in the workspace.
-  int ns = bwd_split_ways(s);
-  const size_t split_bytes = (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * D * sizeof(float);
-  if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes ||
-                 (reinterpret_cast<uintptr_t>(ws) & 15u) != 0))
-    ns = 1;  // the partial tiles are written and read 16 bytes at a time
+  const BwdPlan pl = bwd_plan(s, ws_bytes, (reinterpret_cast<uintptr_t>(ws) & 15u) == 0);
+  const int ns = pl.ns;
   const long long tiles = (long long)(s.Nq / 64) * s.BH;  // 64-row tiles (when ns > 1)
+  // Partial sums of split grids follow the two per-row arrays in the workspace.
   float* kvpart = const_cast<float*>(ws) + 2 * rows;
   float* qpart = kvpart + (size_t)tiles * ns * 2 * 64 * D;  // after dK^T, dV^T of every tile
   bool launched = false;
-  // Paired only where the plain grid (two 128-row tiles per head per 128 rows) would leave
-  // the longest tile on the critical path of a small grid (up to three paired workgroups per
-  // CU, measured faster than the plain kernel there); see bwd_causal_paired_kernel.
-  // (d = 128 grids at this size are rare, and hipcc 7.2 cannot register-allocate that
-  // instantiation, so it is not built.)
   if constexpr (CAUSAL && D >= 32 && D <= 64) {
-    if (bwd_uses_paired(s)) {
+    if (pl.kernel == kBwdPaired) {
       hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(tiles * ns)), dim3(256),
                          0, stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
                          (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
@@ -1764,6 +1792,27 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   }
   return hipGetLastError();
 }
+
+// Kernel names as a profiler lists them, indexed by d (16, 32, 64, 128) and mask.
+int d_index(int d) { return d == 16 ? 0 : d == 32 ? 1 : d == 64 ? 2 : 3; }
+const char* const kFwdPlainNames[2][4] = {
+    {"fwd_kernel<16, false>", "fwd_kernel<32, false>", "fwd_kernel<64, false>",
+     "fwd_kernel<128, false>"},
+    {"fwd_kernel<16, true>", "fwd_kernel<32, true>", "fwd_kernel<64, true>",
+     "fwd_kernel<128, true>"}};
+const char* const kFwdPairedNames[4] = {"", "fwd_causal_paired_kernel<32>",
+                                        "fwd_causal_paired_kernel<64>",
+                                        "fwd_causal_paired_kernel<128>"};
+const char* const kFwdSplitNames[4] = {"fwd_causal_split_kernel<16>",
+                                       "fwd_causal_split_kernel<32>",
+                                       "fwd_causal_split_kernel<64>", ""};
+const char* const kBwdPlainNames[2][4] = {
+    {"bwd_kernel<16, false>", "bwd_kernel<32, false>", "bwd_kernel<64, false>",
+     "bwd_kernel<128, false>"},
+    {"bwd_kernel<16, true>", "bwd_kernel<32, true>", "bwd_kernel<64, true>",
+     "bwd_kernel<128, true>"}};
+const char* const kBwdPairedNames[4] = {"", "bwd_causal_paired_kernel<32>",
+                                        "bwd_causal_paired_kernel<64>", ""};
 
 }  // namespace
 
@@ -1853,6 +1902,21 @@ hipError_t bwd_atomic_t(const Shape& s, const void* Q, const void* K, const void
   return hipGetLastError();
 }
 }  // namespace
+
+const char* fwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes) {
+  const FwdPlan pl = fwd_plan(s, workspace_bytes);
+  const int di = d_index(s.d);
+  if (pl.kernel == kFwdSplit) return kFwdSplitNames[di];
+  if (pl.kernel == kFwdPaired) return kFwdPairedNames[di];
+  return kFwdPlainNames[s.causal ? 1 : 0][di];
+}
+
+const char* bwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes) {
+  const BwdPlan pl = bwd_plan(s, workspace_bytes, true);
+  const int di = d_index(s.d);
+  if (pl.kernel == kBwdPaired) return kBwdPairedNames[di];
+  return kBwdPlainNames[s.causal ? 1 : 0][di];
+}
 
 size_t bwd_atomic_workspace_bytes_bf16(const Shape& s) {
   return (size_t)s.BH * (size_t)s.Nq * (2 + (size_t)s.d) * sizeof(float);

@@ -601,6 +601,26 @@ size_t bwd_split_workspace_bytes_f32(const Shape& s) {
   return (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
 }
 
+const char* fwd_kernel_name_f32(const Shape& s) {
+  static const char* const names[2][4] = {
+      {"fwd_f32_kernel<16, false>", "fwd_f32_kernel<32, false>", "fwd_f32_kernel<64, false>",
+       "fwd_f32_kernel<128, false>"},
+      {"fwd_f32_kernel<16, true>", "fwd_f32_kernel<32, true>", "fwd_f32_kernel<64, true>",
+       "fwd_f32_kernel<128, true>"}};
+  const int di = s.d == 16 ? 0 : s.d == 32 ? 1 : s.d == 64 ? 2 : 3;
+  return names[s.causal ? 1 : 0][di];
+}
+
+const char* bwd_kernel_name_f32(const Shape& s) {
+  static const char* const names[2][4] = {
+      {"bwd_f32_kernel<16, false>", "bwd_f32_kernel<32, false>", "bwd_f32_kernel<64, false>",
+       "bwd_f32_kernel<128, false>"},
+      {"bwd_f32_kernel<16, true>", "bwd_f32_kernel<32, true>", "bwd_f32_kernel<64, true>",
+       "bwd_f32_kernel<128, true>"}};
+  const int di = s.d == 16 ? 0 : s.d == 32 ? 1 : s.d == 64 ? 2 : 3;
+  return names[s.causal ? 1 : 0][di];
+}
+
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           float* O, float* L, float* workspace, size_t workspace_bytes,
                           hipStream_t stream) {

@@ -43,11 +43,18 @@ size_t bwd_atomic_workspace_bytes_bf16(const Shape& s);
 hipError_t launch_bwd_atomic_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                                   const void* dO, void* dQ, void* dK, void* dV, float* workspace,
                                   hipStream_t stream);
+// Names of the main forward and backward kernels the launchers above run for these arguments
+// and workspace sizes, as a profiler lists them (the launchers and these take the same plan).
+const char* fwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes);
+const char* bwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes);
 // fp32: small grids likewise spread each workgroup's key (forward) or step (backward) range
 // over several workgroups when the workspace holds fwd_workspace_bytes_f32 or
 // bwd_split_workspace_bytes_f32 bytes; otherwise they run unsplit (fp32 needs no workspace).
 size_t fwd_workspace_bytes_f32(const Shape& s);
 size_t bwd_split_workspace_bytes_f32(const Shape& s);
+// fp32 runs one forward and one backward kernel for every grid (plus a merge launch when split).
+const char* fwd_kernel_name_f32(const Shape& s);
+const char* bwd_kernel_name_f32(const Shape& s);
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
                           float* O, float* L, float* workspace, size_t workspace_bytes,
                           hipStream_t stream);

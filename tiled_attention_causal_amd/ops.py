@@ -83,15 +83,18 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: boo
         need = _forward_ws_bytes(_DTYPES[q.dtype], B, H, Nq, Nk, d, int(bool(is_causal)))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = 0, 0
-    if workspace is not None:
+    args = (_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            int(bool(is_causal)), sc, out.data_ptr(), lse.data_ptr())
+    if workspace is None:
+        st = lib.fa_forward(*args, _stream_ptr(q))
+        _raise(st, "fa_forward")
+    else:
         if workspace.device != q.device or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on q's device")
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    st = lib.fa_forward(_DTYPES[q.dtype], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
-                        v.data_ptr(), int(bool(is_causal)), sc, out.data_ptr(), lse.data_ptr(),
-                        ws_ptr or None, ws_bytes, _stream_ptr(q))
-    _raise(st, "fa_forward")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        st = lib.fa_forward_with_workspace(*args, workspace.data_ptr() if ws_bytes else None,
+                                           ws_bytes, _stream_ptr(q))
+        _raise(st, "fa_forward_with_workspace")
     return out, lse
 
 
@@ -116,8 +119,9 @@ def _backward_args(q, k, v, o, lse, do, dq, dk, dv, workspace):
         # bf16 needs two floats per query row; fa_backward_workspace_bytes may ask for more
         # (partial sums that let small causal grids use every CU), which is optional.
         need = B * H * Nq * 8 if dt == torch.bfloat16 else 0
-        if workspace.device != q.device or workspace.nbytes < need:
-            raise ValueError(f"workspace must be a tensor of at least {need} bytes "
+        if (workspace.device != q.device or workspace.nbytes < need
+                or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes "
                              f"({ws_bytes} for the fastest path) on {q.device}")
         ws, ws_bytes = workspace, workspace.nbytes
     else:
@@ -152,10 +156,11 @@ def fa_backward_preprocess(o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor,
     B, H, Nq, d = o.shape
     if o.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {o.dtype}")
+    _check("o", o, (B, H, Nq, d), o.dtype, o.device)
     _check("do", do, (B, H, Nq, d), o.dtype, o.device)
     _check("lse", lse, (B, H, Nq), torch.float32, o.device)
-    if workspace.device != o.device:
-        raise ValueError(f"workspace must be on {o.device}")
+    if workspace.device != o.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {o.device}")
     st = lib.fa_backward_preprocess(_DTYPES[o.dtype], B, H, Nq, d, o.data_ptr(), lse.data_ptr(),
                                     do.data_ptr(), workspace.data_ptr(), workspace.nbytes,
                                     _stream_ptr(o))
@@ -215,6 +220,18 @@ def fa_backward_atomic(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
                                 dv.data_ptr(), ws.data_ptr(), ws_bytes, _stream_ptr(q))
     _raise(st, "fa_backward_atomic")
     return dq, dk, dv
+
+
+def kernel_names(dtype: torch.dtype, B: int, H: int, Nq: int, Nk: int, d: int, is_causal: bool,
+                 forward_workspace_bytes: int = 0, backward_workspace_bytes: int = 0):
+    """(forward, backward) names of the attention kernels the library launches for these
+    arguments and workspace sizes, from the library's own dispatch (fa_forward_kernel_name,
+    fa_backward_kernel_name)."""
+    lib = _lib.load()
+    dt = _DTYPES[dtype]
+    c = int(bool(is_causal))
+    return (lib.fa_forward_kernel_name(dt, B, H, Nq, Nk, d, c, forward_workspace_bytes).decode(),
+            lib.fa_backward_kernel_name(dt, B, H, Nq, Nk, d, c, backward_workspace_bytes).decode())
 
 
 class FlashAttention(torch.autograd.Function):
