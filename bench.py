@@ -6,11 +6,15 @@ in HBM before the timed region starts. Counted work (the metric's convention): f
 4*B*H*N^2*d FLOPs, halved when causal; backward 2.5x forward.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-configs]
 
-The defaults (W = 500, K = 2000) let the GPU reach its steady clock first: the first hundred
-or so steps of this work run 10-25% slower. Prints one JSON line. Extra modes:
+One JSON line. The run first measures every workload (`configs`): fa_forward, fa_backward
+and both back to back, each timed with HIP events over 100 repetitions (20 for the 16384-row
+workload) with a 512 MiB write before every repetition to flush L2 and the MALL (median,
+p10, p90), plus one warm-cache figure; then the headline: W untimed steps and K timed steps
+of the headline workload, back to back. The per-config block takes several seconds of GPU
+work, so the headline runs at the clock the GPU holds under sustained load. Extra modes:
     --copy-calibration   run only a plain device copy of known size (HBM counter scaling)
-    --all                also print a per-workload table to stderr
     --sweep              forward / backward / end-to-end latency of these kernels against
                          plain PyTorch attention over sequence length x head dim x dtype
                          (a markdown table on stdout, no JSON line)
@@ -31,8 +35,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PUBLISHED_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, as published
 PEAK_HBM_GBPS = 8000.0
+MFMA_BF16_FLOP_PER_CLK_PER_CU = 4096  # 4 SIMDs x one 32x32x16 MFMA (32768 FLOP) per 32 clk
 DEFAULT_WORKLOAD = "b8_n4096_d64"
 KERNEL_SOURCES = ["tiled_attention_causal_amd/csrc/fa_bf16.hip",
                   "tiled_attention_causal_amd/csrc/fa_common.h"]
@@ -43,12 +48,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload flushed-cache block")
+    ap.add_argument("--config-reps", type=int, default=100,
+                    help="repetitions per measurement in the per-workload block (a fifth "
+                         "of that for the 16384-row workload)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="run the oracle sample for at least this much CPU time")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--all", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--e2e", action="store_true",
                     help="training-step time of a toy decoder, plain vs flash attention")
@@ -74,30 +83,42 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_names(w):
-    """Names of the main forward and backward kernels the library launches for workload `w`,
-    following the dispatch rules of fa_bf16.hip and fa_f32.hip. Square causal grids of
-    128-row tiles that fit the chip in one wave of workgroups take the split forward
-    (d <= 64) or the paired forward (d = 128); at d = 32 and 64 the paired kernels also take
-    grids of up to two (forward) or three (backward) of their workgroups per CU."""
-    c = "true" if w.causal else "false"
-    if w.dtype == "f32":
-        return f"fwd_f32_kernel<{w.d}, {c}>", f"bwd_f32_kernel<{w.d}, {c}>"
-    n_cus = 256
-    square = w.causal and w.Nq == w.Nk and w.Nq % 128 == 0
-    paired_d = 32 <= w.d <= 64
-    pairs = (w.Nq // 128) * w.B * w.H
-    if square and pairs <= n_cus:
-        fwd = (f"fwd_causal_split_kernel<{w.d}>" if w.d <= 64
-               else f"fwd_causal_paired_kernel<{w.d}>")
-    elif square and paired_d and pairs <= 2 * n_cus:
-        fwd = f"fwd_causal_paired_kernel<{w.d}>"
-    else:
-        fwd = f"fwd_kernel<{w.d}, {c}>"
-    bwd = (f"bwd_causal_paired_kernel<{w.d}>"
-           if square and paired_d and (w.Nq // 64) * w.B * w.H <= 3 * n_cus
-           else f"bwd_kernel<{w.d}, {c}>")
-    return fwd, bwd
+def kernel_names(w, fwd_ws_bytes=0, bwd_ws_bytes=0):
+    """(forward, backward) names of the attention kernels the library launches for workload
+    `w` with these workspace sizes, from the library's own dispatch."""
+    from seeded_inputs import torch_dtype
+    from tiled_attention_causal_amd import kernel_names as lib_names
+    return lib_names(torch_dtype(w.dtype), w.B, w.H, w.Nq, w.Nk, w.d, w.causal, fwd_ws_bytes,
+                     bwd_ws_bytes)
+
+
+def _loaded_hip_runtime():
+    """The HIP runtime library this process already uses (so no second copy is loaded)."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in os.path.basename(path):
+                return ctypes.CDLL(path)
+    return ctypes.CDLL("libamdhip64.so")
+
+
+def device_peak(dev_index=0):
+    """bf16 dense MFMA peak of the device: compute units x peak engine clock x 4096 FLOP per
+    clock per CU, from hipDeviceGetAttribute (hipDeviceAttributeMultiprocessorCount = 63,
+    hipDeviceAttributeClockRate = 5, in kHz)."""
+    import ctypes
+    hip = _loaded_hip_runtime()
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    if (hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, dev_index) != 0
+            or hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, dev_index) != 0):
+        raise RuntimeError("hipDeviceGetAttribute failed")
+    tflops = cus.value * khz.value * 1e3 * MFMA_BF16_FLOP_PER_CLK_PER_CU / 1e12
+    return {"bf16_tflops": round(tflops, 1), "compute_units": cus.value,
+            "peak_clock_mhz": khz.value / 1000.0,
+            "formula": f"{cus.value} CUs x {khz.value / 1000.0:g} MHz x "
+                       f"{MFMA_BF16_FLOP_PER_CLK_PER_CU} FLOP/clk/CU",
+            "published_bf16_tflops": PUBLISHED_PEAK_BF16_TFLOPS}
 
 
 def read_traffic(workload: str, kernel: str):
@@ -121,36 +142,129 @@ def read_traffic(workload: str, kernel: str):
         return None
 
 
-def time_workload(w, steps, warmup):
+class Workspace:
+    """Device tensors and pre-marshalled C-ABI calls for one workload: forward (fa_forward,
+    or fa_forward_with_workspace where the workload can use a workspace), the backward as
+    fa_backward, and its two steps fa_backward_preprocess and fa_backward_main. Calls go
+    straight through ctypes, so the host enqueues a launch in a few microseconds."""
+
+    def __init__(self, w):
+        import torch
+        from seeded_inputs import workload_inputs
+        from tiled_attention_causal_amd import (_lib, backward_workspace_bytes,
+                                                forward_workspace_bytes)
+        self.w = w
+        dev = torch.device("cuda:0")
+        inp = workload_inputs(w)
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        self.fws_bytes = forward_workspace_bytes(q, k, w.causal)
+        self.bws_bytes = backward_workspace_bytes(q, k)
+        fws = torch.empty(max(1, self.fws_bytes), dtype=torch.uint8, device=dev)
+        bws = torch.empty(max(1, self.bws_bytes), dtype=torch.uint8, device=dev)
+        self.tensors = (q, k, v, do, o, lse, dq, dk, dv, fws, bws)  # kept alive
+        self.stream = torch.cuda.current_stream(dev)
+        lib = _lib.load()
+        self.ok = _lib.FA_SUCCESS
+        self.err = _lib.FAError
+        dt = _lib.FA_DTYPE_BF16 if w.dtype == "bf16" else _lib.FA_DTYPE_F32
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
+        sp = self.stream.cuda_stream
+        causal = int(bool(w.causal))
+        fa = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), causal, w.scale,
+              o.data_ptr(), lse.data_ptr())
+        if self.fws_bytes:
+            self.fwd = (lib.fa_forward_with_workspace, fa + (fws.data_ptr(), self.fws_bytes, sp))
+        else:
+            self.fwd = (lib.fa_forward, fa + (sp,))
+        bw = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+              lse.data_ptr(), do.data_ptr(), causal, w.scale, dq.data_ptr(), dk.data_ptr(),
+              dv.data_ptr(), bws.data_ptr(), self.bws_bytes, sp)
+        self.bwd = (lib.fa_backward, bw)
+        self.prep = (lib.fa_backward_preprocess,
+                     (dt, B, H, Nq, d, o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      bws.data_ptr(), self.bws_bytes, sp))
+        self.main = (lib.fa_backward_main, bw)
+
+    def call(self, which):
+        fn, a = which
+        st = fn(*a)
+        if st != self.ok:
+            raise self.err(st, fn.__name__)
+
+    def step(self):
+        self.call(self.fwd)
+        self.call(self.bwd)
+
+
+def _pct(ts, p):
+    import numpy as np
+    return float(np.percentile(np.asarray(ts), p))
+
+
+def config_block(ws, reps, flush):
+    """Flushed-cache medians (p10, p90) of fa_forward, fa_backward and both, over `reps`
+    repetitions after 10 warm-up steps, each repetition preceded by a 512 MiB write that
+    evicts L2 and the MALL (as triton.testing.do_bench clears the cache), plus the warm
+    figure: the mean step of 5 chunks of 20 back-to-back steps, median chunk."""
     import torch
-    from seeded_inputs import workload_inputs
-    from tiled_attention_causal_amd import (backward_workspace_bytes, fa_backward,
-                                            fa_backward_main, fa_backward_preprocess,
-                                            fa_forward, forward_workspace_bytes)
+    w = ws.w
+    fl = w.counted_flops()
+    for _ in range(10):
+        ws.step()
+    torch.cuda.synchronize()
+    out = {"workload": w.name, "reps": reps,
+           "kernels": dict(zip(("fwd", "bwd"), kernel_names(w, ws.fws_bytes, ws.bws_bytes)))}
+    runs = {"fwd": (lambda: ws.call(ws.fwd), fl["fwd"]),
+            "bwd": (lambda: ws.call(ws.bwd), fl["bwd"]),
+            "fwd_bwd": (ws.step, fl["total"])}
+    for name, (fn, flops) in runs.items():
+        ev = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(ws.stream)
+            fn()
+            e1.record(ws.stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in ev]
+        med = _pct(ts, 50)
+        out[name] = {"median_ms": round(med, 5), "p10_ms": round(_pct(ts, 10), 5),
+                     "p90_ms": round(_pct(ts, 90), 5),
+                     "tflops": round(flops / (med * 1e-3) / 1e12, 2)}
+    chunks = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ws.stream)
+        for _ in range(20):
+            ws.step()
+        e1.record(ws.stream)
+        chunks.append((e0, e1))
+    torch.cuda.synchronize()
+    warm = sorted(a.elapsed_time(b) / 20 for a, b in chunks)[2]
+    out["warm_fwd_bwd"] = {"ms": round(warm, 5),
+                           "tflops": round(fl["total"] / (warm * 1e-3) / 1e12, 2),
+                           "label": "warm cache: back-to-back steps, no flush"}
+    return out
 
-    dev = torch.device("cuda:0")
-    inp = workload_inputs(w)
-    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(1, backward_workspace_bytes(q, k)), dtype=torch.uint8, device=dev)
-    fws = torch.empty(forward_workspace_bytes(q, k, w.causal), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
-    def step():
-        fa_forward(q, k, v, w.causal, w.scale, out=o, lse=lse, workspace=fws)
-        fa_backward(q, k, v, o, lse, do, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
-
+def time_workload(ws, steps, warmup):
+    """The headline: `warmup` untimed steps, then exactly `steps` steps between two
+    synchronisations (wall clock), then per-launch HIP-event durations of the step's three
+    launches for the roofline."""
+    import torch
+    w = ws.w
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize(dev)
-
-    # Whole-step wall time over exactly `steps` steps.
+        ws.step()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
-    torch.cuda.synchronize(dev)
+        ws.step()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # Per-launch durations with HIP events on the stream the kernels run on. Each of the
@@ -158,42 +272,21 @@ def time_workload(w, steps, warmup):
     # fa_backward_preprocess and fa_backward_main, exactly what fa_backward enqueues) is
     # repeated back to back between two events, in chunks of CHUNK launches, until `steps`
     # launches of each are timed; a chunk's elapsed time over CHUNK is the kernel's average
-    # launch duration. The launches go through the C ABI with their arguments marshalled
-    # once, so the host keeps ahead of even the 4 us preprocessing kernel and the events
-    # time the GPU, not the host's launch rate.
-    from tiled_attention_causal_amd import _lib
-    lib = _lib.load()
-    dt = _lib.FA_DTYPE_BF16 if w.dtype == "bf16" else _lib.FA_DTYPE_F32
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
-    sp = stream.cuda_stream
-    causal = int(bool(w.causal))
-    fa = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), causal, w.scale,
-          o.data_ptr(), lse.data_ptr(), fws.data_ptr() if fws.numel() else None, fws.numel(),
-          sp)
-    pa = (dt, B, H, Nq, d, o.data_ptr(), lse.data_ptr(), do.data_ptr(), ws.data_ptr(),
-          ws.numel(), sp)
-    ma = (dt, B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-          lse.data_ptr(), do.data_ptr(), causal, w.scale, dq.data_ptr(), dk.data_ptr(),
-          dv.data_ptr(), ws.data_ptr(), ws.numel(), sp)
-    launches = [(lib.fa_forward, fa), (lib.fa_backward_preprocess, pa),
-                (lib.fa_backward_main, ma)]
+    # launch duration, so the events time the GPU, not the host's launch rate.
+    launches = [ws.fwd, ws.prep, ws.main]
     CHUNK = 20
     nchunks = max(1, steps // CHUNK)
     per = [[] for _ in launches]
-    torch.cuda.synchronize(dev)
     for _ in range(nchunks):
-        for i, (fn, a) in enumerate(launches):
+        for i, which in enumerate(launches):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            e0.record(ws.stream)
             for _ in range(CHUNK):
-                st = fn(*a)
-                if st != _lib.FA_SUCCESS:
-                    raise _lib.FAError(st, fn.__name__)
-            e1.record(stream)
+                ws.call(which)
+            e1.record(ws.stream)
             per[i].append((e0, e1))
-    torch.cuda.synchronize(dev)
+    torch.cuda.synchronize()
 
     def stat(i):
         t = sorted(a.elapsed_time(b) / CHUNK for a, b in per[i])
@@ -201,15 +294,16 @@ def time_workload(w, steps, warmup):
 
     (fwd_mean, fwd_med), (prep_mean, prep_med), (main_mean, main_med) = (
         stat(0), stat(1), stat(2))
-    bwd_mean, bwd_med = prep_mean + main_mean, prep_med + main_med
+    names = kernel_names(w, ws.fws_bytes, ws.bws_bytes)
     return {
         "ms_per_step": wall * 1e3 / steps,
         "fwd_ms_mean": fwd_mean,
-        "bwd_ms_mean": bwd_mean,
+        "bwd_ms_mean": prep_mean + main_mean,
         "prep_ms_mean": prep_mean,
         "bwd_main_ms_mean": main_mean,
         "fwd_ms_median": fwd_med,
-        "bwd_ms_median": bwd_med,
+        "bwd_ms_median": prep_med + main_med,
+        "kernels": names,
     }
 
 
@@ -242,7 +336,10 @@ def cpu_baseline(w, min_s, budget_s):
             break
     flops = w.counted_flops()["total"] * done / len(heads)
     del np
+    # `cores`: the threads the oracle's work actually ran on (its BLAS pool; its elementwise
+    # steps run on one of them). The host's cores available to this process are given apart.
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "blas_threads": int(threads), "host_cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"{done} head passes over the {len(heads)} heads of the workload (one "
                       f"head: B=1,H=1,N={w.Nq},d={w.d}), fp64 forward + backward, {el:.1f} s; "
@@ -581,25 +678,39 @@ def main():
         atomic_dq(args)
         return
 
+    peak = device_peak()
+    peak_tf = peak["bf16_tflops"]
     w = WORKLOADS[args.workload]
+    # Every workload's inputs are drawn and placed on the GPU before anything is timed, so
+    # the GPU runs the measurements back to back: after even a fraction of a second idle it
+    # drops its clock and takes some milliseconds of work to regain it.
+    spaces = {w.name: Workspace(w)}
+    configs = None
+    if not args.no_configs:
+        for name, ww in WORKLOADS.items():
+            if name not in spaces:
+                spaces[name] = Workspace(ww)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        torch.cuda.synchronize()
+        configs = []
+        for name, ww in WORKLOADS.items():
+            reps = max(1, args.config_reps // 5) if ww.Nq >= 16384 else args.config_reps
+            c = config_block(spaces[name], reps, flush)
+            configs.append(c)
+            print(f"{name:18s} flushed median fwd {c['fwd']['median_ms']:.4f} ms, bwd "
+                  f"{c['bwd']['median_ms']:.4f} ms, fwd+bwd {c['fwd_bwd']['median_ms']:.4f} ms "
+                  f"({c['fwd_bwd']['tflops']:.1f} TF/s); warm {c['warm_fwd_bwd']['ms']:.4f} ms",
+                  file=sys.stderr, flush=True)
+        del flush
+
     fl = w.counted_flops()
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(spaces[w.name], args.steps, args.warmup)
     value = fl["total"] / (r["ms_per_step"] * 1e-3) / 1e12
     bwd_tf = fl["bwd"] / (r["bwd_ms_mean"] * 1e-3) / 1e12
     main_tf = fl["bwd"] / (r["bwd_main_ms_mean"] * 1e-3) / 1e12
     fwd_tf = fl["fwd"] / (r["fwd_ms_mean"] * 1e-3) / 1e12
+    fwd_name, bwd_name = r["kernels"]
 
-    if args.all:
-        for name, ww in WORKLOADS.items():
-            rr = time_workload(ww, max(5, args.steps // 5), max(3, args.warmup // 5))
-            f2 = ww.counted_flops()
-            print(f"{name:18s} fwd {rr['fwd_ms_median']:.4f} ms "
-                  f"({f2['fwd'] / rr['fwd_ms_median'] / 1e9:.1f} TF/s)  bwd "
-                  f"{rr['bwd_ms_median']:.4f} ms ({f2['bwd'] / rr['bwd_ms_median'] / 1e9:.1f} TF/s)"
-                  f"  step {rr['ms_per_step']:.4f} ms "
-                  f"({f2['total'] / rr['ms_per_step'] / 1e9:.1f} TF/s)", file=sys.stderr)
-
-    fwd_name, bwd_name = kernel_names(w)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds, 3.0 * args.cpu_seconds)
@@ -617,19 +728,23 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / peak_tf, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype},
+        "peak": peak,
         "passes": {"fwd_kernel": fwd_name, "fwd_ms": round(r["fwd_ms_mean"], 5),
                    "fwd_tflops": round(fwd_tf, 2), "bwd_kernel": bwd_name,
                    "bwd_ms": round(r["bwd_ms_mean"], 5), "bwd_tflops": round(bwd_tf, 2),
                    "bwd_preprocess_ms": round(r["prep_ms_mean"], 5),
                    "bwd_main_ms": round(r["bwd_main_ms_mean"], 5)},
         "roofline": {"kernel": bwd_name, "bound": "mfma", "achieved": round(main_tf, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
+                     "peak": peak_tf, "unit": "TFLOP/s",
+                     "frac": round(main_tf / peak_tf, 4),
                      "traffic": read_traffic(w.name, bwd_name)},
         "cpu_baseline": cpu,
+        "configs": configs,
+        "order": ("per-workload flushed block, then the headline's warm-up and timed steps"
+                  if configs is not None else "headline only"),
     }
     print(json.dumps(out))
 

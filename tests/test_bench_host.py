@@ -1,6 +1,6 @@
 """Host-side checks of bench.py: the plain-attention baseline of the sweep computes attention
-(checked against the oracle on the CPU in float64), the kernel-name table follows the
-dispatch rules, and more than one GPU is refused."""
+(checked against the oracle on the CPU in float64), the kernel names it reports are the
+library's dispatch choices for the workloads, and more than one GPU is refused."""
 import os
 import subprocess
 import sys
