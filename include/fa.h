@@ -22,8 +22,9 @@
  * accumulation is float32 in every case. Data pointers must be 16-byte aligned.
  *
  * Ownership: every pointer is a device pointer owned by the caller. The library allocates
- * and frees nothing, keeps no state between calls and is re-entrant. Outputs must not alias
- * inputs.
+ * and frees nothing, keeps no state between calls and is re-entrant; the one exception is
+ * fa_backward_noalloc, whose workspace is a static device array (see there). Outputs must
+ * not alias inputs.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its kernels on
  * `stream` (NULL means the default stream) and returns. Results are ready
@@ -70,7 +71,8 @@ typedef enum fa_status {
   FA_SUCCESS = 0,
   FA_ERROR_INVALID_VALUE = 1,
   FA_ERROR_NOT_SUPPORTED = 2,
-  FA_ERROR_LAUNCH_FAILED = 3
+  FA_ERROR_LAUNCH_FAILED = 3,
+  FA_ERROR_SCRATCH_TOO_SMALL = 4  /* fa_backward_noalloc: the sizes need more than its array */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -236,6 +238,41 @@ FA_API fa_status fa_backward_atomic(fa_dtype dtype, int64_t B, int64_t H, int64_
                                     const void* dO, int is_causal, float scale, void* dQ,
                                     void* dK, void* dV, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the static device array fa_backward_noalloc keeps its workspace in, per GPU. */
+#define FA_BACKWARD_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+
+/*
+ * fa_backward_noalloc -- fa_backward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments as fa_backward without the workspace, same computation and bitwise the
+ * same results as fa_backward given FA_BACKWARD_NOALLOC_MAX_BYTES bytes of workspace. The
+ * workspace is instead a file-scope static device array of that size inside the library,
+ * one per GPU, which the GPU holds from the first call on it until the process ends; the
+ * call itself allocates nothing (no hipMalloc, hipFree or allocating library routine). On
+ * the first call on a device the library takes the array's address on that device (the
+ * stream's device) with hipGetSymbolAddress and keeps it.
+ *
+ * Limits: bf16 needs B * H * Nq * 8 bytes of it (the per-row terms); sizes needing more
+ * than FA_BACKWARD_NOALLOC_MAX_BYTES return FA_ERROR_SCRATCH_TOO_SMALL before anything is
+ * enqueued. Small square grids use the rest for the partial sums that spread their work
+ * over more workgroups when those fit, and otherwise run unsplit, as fa_backward does with
+ * too little workspace. fp32 uses the array only for those partial sums.
+ *
+ * Sharing: every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents; a call reads only what it wrote earlier in the same call, so nothing needs
+ * clearing. Calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering between their streams) race on the array and must not be
+ * issued; calls on one stream are ordered and safe. Errors as for fa_backward, plus
+ * FA_ERROR_SCRATCH_TOO_SMALL, and FA_ERROR_LAUNCH_FAILED when the array's address cannot
+ * be obtained.
+ */
+FA_API fa_status fa_backward_noalloc(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
+                                     int64_t Nk, int64_t d, const void* Q, const void* K,
+                                     const void* V, const void* O, const float* L,
+                                     const void* dO, int is_causal, float scale, void* dQ,
+                                     void* dK, void* dV, hipStream_t stream);
 
 /*
  * fa_forward_kernel_name, fa_backward_kernel_name -- the name, as a profiler lists it, of the

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == ["fa_backward", "fa_backward_atomic",
                                   "fa_backward_atomic_workspace_bytes",
                                   "fa_backward_kernel_name", "fa_backward_main",
+                                  "fa_backward_noalloc",
                                   "fa_backward_preprocess", "fa_backward_workspace_bytes",
                                   "fa_forward", "fa_forward_kernel_name",
                                   "fa_forward_with_workspace", "fa_forward_workspace_bytes",
@@ -105,7 +106,7 @@ def test_only_the_c_abi_is_exported():
 
 def test_status_strings(lib):
     names = {0: "FA_SUCCESS", 1: "FA_ERROR_INVALID_VALUE", 2: "FA_ERROR_NOT_SUPPORTED",
-             3: "FA_ERROR_LAUNCH_FAILED"}
+             3: "FA_ERROR_LAUNCH_FAILED", 4: "FA_ERROR_SCRATCH_TOO_SMALL"}
     for code, name in names.items():
         assert lib.fa_status_string(code).decode() == name
     assert lib.fa_status_string(77).decode() == "FA_UNKNOWN_STATUS"
@@ -330,3 +331,33 @@ def test_kernel_names_follow_dispatch(lib):
     assert names(0, 1, 1, 128, 128, 16, 1) == ("fwd_f32_kernel<16, true>",
                                                "bwd_f32_kernel<16, true>")
     assert names(1, 1, 1, 128, 128, 48, 1) == ("", "")     # rejected arguments
+
+
+def bwd_noalloc(lib, dtype=1, B=1, H=1, Nq=128, Nk=128, d=64, q=P, k=P, v=P, o=P, lse=P, do=P,
+                causal=1, scale=0.125, dq=P, dk=P, dv=P):
+    return lib.fa_backward_noalloc(dtype, B, H, Nq, Nk, d, q, k, v, o, lse, do, causal, scale,
+                                   dq, dk, dv, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 2), (dict(d=24), 2), (dict(Nk=0), 1), (dict(q=None), 1), (dict(dk=BAD), 1),
+    (dict(scale=math.nan), 1), (dict(lse=None), 1), (dict(do=None), 1),
+    # bf16 needs B*H*Nq*8 bytes of the 32 MiB array: 2 * 2^22 rows need 64 MiB
+    (dict(B=2, Nq=1 << 22, Nk=1 << 22), 4),
+    (dict(B=1, H=3, Nq=1 << 21, Nk=64), 4),
+])
+def test_backward_noalloc_rejects_before_any_gpu_call(lib, kw, code):
+    assert bwd_noalloc(lib, **kw) == code
+
+
+def test_backward_noalloc_limit_and_empty(lib):
+    from tiled_attention_causal_amd import _lib
+    assert _lib.FA_BACKWARD_NOALLOC_MAX_BYTES == 32 << 20
+    assert "FA_BACKWARD_NOALLOC_MAX_BYTES ((size_t)32 << 20)" in open(HEADER).read()
+    assert lib.fa_status_string(4).decode() == "FA_ERROR_SCRATCH_TOO_SMALL"
+    # exactly at the limit the sizes pass validation (the fake pointers then fail it)
+    assert bwd_noalloc(lib, B=1, Nq=1 << 22, Nk=1 << 22, q=None) == 1
+    # nothing to do returns before the array's address is looked up
+    assert bwd_noalloc(lib, B=0) == 0
+    assert bwd_noalloc(lib, Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None,
+                       dq=None, dk=None, dv=None) == 0

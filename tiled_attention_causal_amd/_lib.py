@@ -15,6 +15,8 @@ FA_SUCCESS = 0
 FA_ERROR_INVALID_VALUE = 1
 FA_ERROR_NOT_SUPPORTED = 2
 FA_ERROR_LAUNCH_FAILED = 3
+FA_ERROR_SCRATCH_TOO_SMALL = 4
+FA_BACKWARD_NOALLOC_MAX_BYTES = 32 << 20
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
@@ -44,6 +46,9 @@ SIGNATURES = {
     "fa_backward_main": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr,
                                         _ptr, _ptr, _ptr, _ptr, ctypes.c_int, ctypes.c_float,
                                         _ptr, _ptr, _ptr, _ptr, ctypes.c_size_t, _ptr]),
+    "fa_backward_noalloc": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr,
+                                           _ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_int,
+                                           ctypes.c_float, _ptr, _ptr, _ptr, _ptr]),
     "fa_forward_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                                  ctypes.c_int, ctypes.c_size_t]),
     "fa_backward_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,

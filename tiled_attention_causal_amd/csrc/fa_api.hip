@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
@@ -45,6 +47,47 @@ bool bad_ptr(const void* p) { return p == nullptr || !aligned16(p); }
 
 }  // namespace
 
+// fa_backward_noalloc's workspace: one array per GPU, part of the library's device code object,
+// so it exists on a device once the library's code is loaded there and lives until the
+// process ends. Host code never uses this name as an address (on the host it is only a
+// stand-in for the symbol): scratch_address() gives each device's address.
+static __device__ __align__(256) unsigned char scratch[FA_BACKWARD_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device, looked up once per device with that
+// device current and kept.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fa_status_string(fa_status status) {
@@ -57,6 +100,8 @@ const char* fa_status_string(fa_status status) {
       return "FA_ERROR_NOT_SUPPORTED";
     case FA_ERROR_LAUNCH_FAILED:
       return "FA_ERROR_LAUNCH_FAILED";
+    case FA_ERROR_SCRATCH_TOO_SMALL:
+      return "FA_ERROR_SCRATCH_TOO_SMALL";
   }
   return "FA_UNKNOWN_STATUS";
 }
@@ -143,13 +188,17 @@ static fa_status check_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq
                                 int64_t d, const void* Q, const void* K, const void* V,
                                 const void* O, const float* L, const void* dO, int is_causal,
                                 float scale, void* dQ, void* dK, void* dV, void* workspace,
-                                size_t workspace_bytes, fa::Shape* s, bool* nothing) {
+                                size_t workspace_bytes, fa::Shape* s, bool* nothing,
+                                bool check_workspace = true) {
   const fa_status st = check_common(dtype, B, H, Nq, Nk, d, scale, is_causal, s);
   if (st != FA_SUCCESS) return st;
   const size_t ws_need = backward_rows_bytes(dtype, *s);
-  if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
-  if (ws_need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
-    return FA_ERROR_INVALID_VALUE;
+  if (check_workspace) {
+    if (workspace_bytes < ws_need) return FA_ERROR_INVALID_VALUE;
+    if (ws_need > 0 &&
+        (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
+      return FA_ERROR_INVALID_VALUE;
+  }
   const bool has_q = (int64_t)s->BH * Nq > 0, has_k = (int64_t)s->BH * Nk > 0;
   *nothing = !has_q && !has_k;
   if (*nothing) return FA_SUCCESS;
@@ -219,6 +268,28 @@ fa_status fa_backward(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t 
   if (st != FA_SUCCESS) return st;
   return fa_backward_main(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale, dQ, dK,
                           dV, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_backward_noalloc(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t d, const void* Q, const void* K, const void* V,
+                              const void* O, const float* L, const void* dO, int is_causal,
+                              float scale, void* dQ, void* dK, void* dV, hipStream_t stream) {
+  fa::Shape s;
+  bool nothing = false;
+  // Every argument is checked before the first HIP call.
+  fa_status st = check_backward(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale,
+                                dQ, dK, dV, nullptr, 0, &s, &nothing, false);
+  if (st != FA_SUCCESS) return st;
+  if (backward_rows_bytes(dtype, s) > FA_BACKWARD_NOALLOC_MAX_BYTES)
+    return FA_ERROR_SCRATCH_TOO_SMALL;
+  if (nothing) return FA_SUCCESS;
+  void* ws = nullptr;
+  if (scratch_address(stream, &ws) != hipSuccess) return FA_ERROR_LAUNCH_FAILED;
+  st = fa_backward_preprocess(dtype, B, H, Nq, d, O, L, dO, ws, FA_BACKWARD_NOALLOC_MAX_BYTES,
+                              stream);
+  if (st != FA_SUCCESS) return st;
+  return fa_backward_main(dtype, B, H, Nq, Nk, d, Q, K, V, O, L, dO, is_causal, scale, dQ, dK,
+                          dV, ws, FA_BACKWARD_NOALLOC_MAX_BYTES, stream);
 }
 
 size_t fa_backward_atomic_workspace_bytes(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,

@@ -183,6 +183,30 @@ def fa_backward_main(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     return dq, dk, dv
 
 
+def fa_backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                        lse: torch.Tensor, do: torch.Tensor, is_causal: bool, scale: float | None,
+                        dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor):
+    """fa_backward with the library's static device workspace instead of one passed in, for
+    callers that cannot allocate: the outputs must be given, and nothing is allocated."""
+    lib = _lib.load()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for name, t, n in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq), ("do", do, Nq),
+                       ("dq", dq, Nq), ("dk", dk, Nk), ("dv", dv, Nk)):
+        _check(name, t, (B, H, n, d), dt, q.device)
+    _check("lse", lse, (B, H, Nq), torch.float32, q.device)
+    sc = default_scale(d) if scale is None else float(scale)
+    st = lib.fa_backward_noalloc(_DTYPES[dt], B, H, Nq, Nk, d, q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                 int(bool(is_causal)), sc, dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), _stream_ptr(q))
+    _raise(st, "fa_backward_noalloc")
+    return dq, dk, dv
+
+
 def backward_workspace_bytes(q: torch.Tensor, k: torch.Tensor) -> int:
     """Bytes of workspace fa_backward needs for these query and key tensors."""
     B, H, Nq, d = q.shape
