@@ -43,11 +43,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Wait until at most K vector-memory instructions of this wave are outstanding (vmcnt(K)):
-// they return in issue order, so this waits for everything but the K most recent.
+// they return in issue order, so this waits for everything but the K most recent. The 6-bit
+// count is split in the encoding: bits 3:0 and 15:14.
 template <int K>
 __device__ __forceinline__ void wait_vmem_keep() {
-  static_assert(K >= 0 && K < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | K);
+  static_assert(K >= 0 && K < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (K & 15) | ((K >> 4) << 14));
 }
 
 // Workgroup barrier that publishes this wave's LDS writes and completes its LDS reads
