@@ -898,9 +898,8 @@ __device__ __forceinline__ void q_step(const bf16* buf, const QOps<D>& op,
     v[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
   if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);  // as in kv_step
-  f32x16 st[1] = {zero16()}, dpt;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dpt[r] = nd;  // dP starts at -D of this lane's query
+  f32x16 st[1] = {zero16()};
+  f32x16 dpt = splat16(nd);  // dP starts at -D of this lane's query
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     st[0] = mfma32(k[s], qf[s], st[0]);

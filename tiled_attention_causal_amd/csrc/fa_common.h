@@ -147,6 +147,24 @@ __device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// An MFMA accumulator with all sixteen registers equal to x, as eight 64-bit moves of one
+// (x, x) pair: the compiler builds the same splat from sixteen or more 32-bit moves. The moves
+// sit in one asm block, which the compiler cannot see as VALU writes, so the block ends with
+// the two wait states an MFMA needs before reading a VGPR that a VALU instruction wrote. The
+// outputs are early-clobber, so none shares a register with the pair.
+__device__ __forceinline__ f32x16 splat16(float x) {
+  typedef double f64x8 __attribute__((ext_vector_type(8)));
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const double p = __builtin_bit_cast(double, u32x2{b, b});
+  double r0, r1, r2, r3, r4, r5, r6, r7;
+  asm("v_mov_b64 %0, %8\n\tv_mov_b64 %1, %8\n\tv_mov_b64 %2, %8\n\tv_mov_b64 %3, %8\n\t"
+      "v_mov_b64 %4, %8\n\tv_mov_b64 %5, %8\n\tv_mov_b64 %6, %8\n\tv_mov_b64 %7, %8\n\t"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(p));
+  return __builtin_bit_cast(f32x16, f64x8{r0, r1, r2, r3, r4, r5, r6, r7});
+}
+
 // x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]) in every lane: after the swap a holds the lower
 // half's value and b the upper half's in every lane, so no lane select is needed and both
 // halves get the bitwise identical result.
