@@ -163,8 +163,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
   // Each iteration issues its transposed V reads before the next tile's direct loads: the
   // compiler cannot tell that they do not alias and would otherwise wait for those loads (the
   // full memory latency) before the reads. Plain LDS reads do not have this problem.
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  // One key tile; buf (0 or 1) holds it. Unrolled by two below so that buf is a constant in
+  // each copy and every LDS address is a fixed register plus an immediate offset.
+  auto step = [&](int kt, int buf) {
     const int k0 = kt * BK;
     const bool active = qw0 < Nq && (!CAUSAL || k0 <= qw0 + 31);
     const bf16* sK = smem + buf * BUF;
@@ -209,6 +210,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(const bf16* __restrict__ Q,
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, 0);
+    if (kt + 1 < nkt) step(kt + 1, 1);
   }
 
   const float lt = halves_sum(l);
@@ -519,11 +524,14 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   wait_vmem();
   __syncthreads();
   const int jmax = (S + NP - 1) / NP;
-  for (int j = 0; j < jmax; ++j) {
+  // One step of the run; b (0 or 1) is the buffer holding its K/V tile. The loop below is
+  // unrolled by two so that b is a constant in each copy: every LDS address is then a fixed
+  // register plus an immediate offset instead of being formed again on every step.
+  auto step = [&](int j, int b) {
     const int n = st + j;
     const bool act = n < en;
-    const bf16* sK = kv[pr][j & 1][0];
-    const bf16* sV = kv[pr][j & 1][1];
+    const bf16* sK = kv[pr][b][0];
+    const bf16* sV = kv[pr][b][1];
     // All of this step's LDS operands are requested before the next tile's direct loads
     // (the compiler would otherwise wait for those loads ahead of the transposed reads).
     bf16x8 vfr[4][DB], kfr[2][DS];
@@ -537,7 +545,7 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
 #pragma unroll
         for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(sK, 32 * kb + l32, 2 * q + g);
     }
-    if (n + 1 < en) fetch(n + 1, (j & 1) ^ 1);
+    if (n + 1 < en) fetch(n + 1, b ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     if (act) {
       const bool isA = n < nA;
@@ -569,6 +577,10 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int j = 0; j < jmax; j += 2) {
+    step(j, 0);
+    if (j + 1 < jmax) step(j + 1, 1);
   }
 
   // Every pair parks its last partial (of A if its run ends within A, else of B) in slot pr.
@@ -1021,9 +1033,11 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
   if (lo < hi) kv_fetch<D, 4>(Qr, dOr, L2r, NDr, lo * 32, smem, w, lane);
   wait_vmem();
   __syncthreads();
-  for (int mt = lo; mt < hi; ++mt) {
-    bf16* buf = smem + ((mt - lo) & 1) * B::KV_BUF;
-    bf16* nbuf = smem + (((mt - lo) & 1) ^ 1) * B::KV_BUF;
+  // One query step; buffer p (0 or 1) holds it. Unrolled by two below so that p is a
+  // constant in each copy and every LDS address is a fixed register plus an immediate.
+  auto step = [&](int mt, int p) {
+    bf16* buf = smem + p * B::KV_BUF;
+    bf16* nbuf = smem + (p ^ 1) * B::KV_BUF;
     const int m0 = mt * 32;
     const bool active = kw0 < Nk && (!CAUSAL || m0 + 31 >= kw0);
     KvOps<D> op;  // unused: transposed operands are read late (see KvOps)
@@ -1033,6 +1047,10 @@ __device__ __forceinline__ void dkdv_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc
                         krow - m0 - 4 * g, lane, l32, g);
     wait_vmem();
     __syncthreads();
+  };
+  for (int mt = lo; mt < hi; mt += 2) {
+    step(mt, 0);
+    if (mt + 1 < hi) step(mt + 1, 1);
   }
 
   if (ns > 1) {  // Nq = Nk, a multiple of 128: every row exists
@@ -1075,9 +1093,10 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
   }
   wait_vmem();
   __syncthreads();
-  for (int kt = lo; kt < hi; ++kt) {
-    const bf16* buf = smem + ((kt - lo) & 1) * B::Q_BUF;
-    bf16* nbuf = smem + (((kt - lo) & 1) ^ 1) * B::Q_BUF;
+  // One key step; buffer p (0 or 1) holds it, unrolled by two as in dkdv_part.
+  auto step = [&](int kt, int p) {
+    const bf16* buf = smem + p * B::Q_BUF;
+    bf16* nbuf = smem + (p ^ 1) * B::Q_BUF;
     const int n0 = kt * 32;
     const bool active = qw0 < Nq && (!CAUSAL || n0 <= qw0 + 31);
     QOps<D> op;  // unused: transposed operands are read late (see KvOps)
@@ -1092,6 +1111,10 @@ __device__ __forceinline__ void dq_part(bf16* smem, rsrc_t Qr, rsrc_t Kr, rsrc_t
                        l32, g);
     wait_vmem();
     __syncthreads();
+  };
+  for (int kt = lo; kt < hi; kt += 2) {
+    step(kt, 0);
+    if (kt + 1 < hi) step(kt + 1, 1);
   }
 
   if (ns > 1) {
