@@ -8,8 +8,8 @@ in HBM before the timed region starts. Counted work (the metric's convention): f
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-configs]
 
-One JSON line. The run first measures every workload (`configs`): fa_forward, fa_backward
-and both back to back, each timed with HIP events over 100 repetitions (20 for the 16384-row
+One JSON line. The run first measures every workload (`configs`, the headline's workload
+last): fa_forward, fa_backward and both back to back, each timed with HIP events over 100 repetitions (20 for the 16384-row
 workload) with a 512 MiB write before every repetition to flush L2 and the MALL (median,
 p10, p90), plus one warm-cache figure; then the headline: W untimed steps and K timed steps
 of the headline workload, back to back. The per-config block takes several seconds of GPU
@@ -693,7 +693,12 @@ def main():
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
         torch.cuda.synchronize()
         configs = []
-        for name, ww in WORKLOADS.items():
+        # The headline's workload goes last, so the headline starts from the clock and cache
+        # state its own back-to-back steps leave (the state a training loop runs in), not
+        # from the power state another workload's warm chunks leave behind.
+        order = [n for n in WORKLOADS if n != w.name] + [w.name]
+        for name in order:
+            ww = WORKLOADS[name]
             reps = max(1, args.config_reps // 5) if ww.Nq >= 16384 else args.config_reps
             c = config_block(spaces[name], reps, flush)
             configs.append(c)
@@ -743,8 +748,8 @@ def main():
                      "traffic": read_traffic(w.name, bwd_name)},
         "cpu_baseline": cpu,
         "configs": configs,
-        "order": ("per-workload flushed block, then the headline's warm-up and timed steps"
-                  if configs is not None else "headline only"),
+        "order": ("per-workload flushed block (the headline's workload last), then the "
+                  "headline's warm-up and timed steps" if configs is not None else "headline only"),
     }
     print(json.dumps(out))
 
