@@ -39,7 +39,7 @@ def test_kernel_names_follow_dispatch():
     assert bench.kernel_names(WORKLOADS["long_n16384_d128"]) == (
         "fwd_kernel<128, true>", "bwd_kernel<128, true>")
     assert bench.kernel_names(WORKLOADS["gpt_small"]) == (
-        "fwd_causal_paired_kernel<64>", "bwd_causal_paired_kernel<64>")
+        "fwd_causal_paired_kernel<64>", "bwd_causal_paired_lean_kernel<64>")
     assert bench.kernel_names(WORKLOADS["xl_causal"]) == (
         "fwd_kernel<64, true>", "bwd_kernel<64, true>")
     assert bench.kernel_names(WORKLOADS["tiny_f32"]) == (

@@ -1354,8 +1354,13 @@ __device__ __forceinline__ void stream3(int first, int last, bf16* __restrict__ 
 //     2(i+1): pair 0 runs A's first T+1 steps, pair 1 runs B and then A's rest.
 // Both pairs make exactly T+1 steps in lockstep, each with its own stream; pair 1 then adds its
 // partial sums for A into pair 0's through LDS.
-template <int D>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel(
+//
+// LEAN reads each step's transposed operands where the products use them instead of up front
+// (kv_step and q_step with EARLY = false), which fits three workgroups per CU (168 VGPRs):
+// bwd_causal_paired_lean_kernel runs grids of two to three workgroups per CU in one round,
+// where two per CU would need a second, half-empty round.
+template <int D, bool LEAN>
+__device__ __forceinline__ void bwd_paired_body(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ L2, const float* __restrict__ ND, const bf16* __restrict__ dO,
     bf16* __restrict__ dQ, bf16* __restrict__ dK, bf16* __restrict__ dV, int N, float scale,
@@ -1426,9 +1431,9 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
           const int kw0 = 64 * kt + 32 * wp;
           if (m0 + 31 >= kw0) {
             KvOps<D> op;
-            op.read(buf, lane);
-            kv_step<D, true>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g,
-                             lane, l32, g);
+            if constexpr (!LEAN) op.read(buf, lane);
+            kv_step<D, !LEAN>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g,
+                              lane, l32, g);
           }
           if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
             if (ns > 1) {
@@ -1528,9 +1533,9 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
           const int qw0 = 64 * qt + 32 * wp;
           if (n0 <= qw0 + 31) {
             QOps<D> op;
-            op.read(buf, lane);
-            q_step<D, true>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
-                            qrow - n0 - 4 * g, lane, l32, g);
+            if constexpr (!LEAN) op.read(buf, lane);
+            q_step<D, !LEAN>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
+                             qrow - n0 - 4 * g, lane, l32, g);
           }
           if (pr == 1 && n + 1 == nB) {  // B is complete: store it and switch to A
             if (ns > 1)
@@ -1576,6 +1581,21 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel
     }
   }
 }
+
+#define FA_PAIRED_ARGS                                                                    \
+  const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,       \
+      const float *__restrict__ L2, const float *__restrict__ ND, const bf16 *__restrict__ dO, \
+      bf16 *__restrict__ dQ, bf16 *__restrict__ dK, bf16 *__restrict__ dV, int N, float scale, \
+      int neg, int ns, float *__restrict__ kvpart, float *__restrict__ qpart
+template <int D>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_causal_paired_kernel(FA_PAIRED_ARGS) {
+  bwd_paired_body<D, false>(Q, K, V, L2, ND, dO, dQ, dK, dV, N, scale, neg, ns, kvpart, qpart);
+}
+template <int D>
+__global__ __launch_bounds__(256, 3) void bwd_causal_paired_lean_kernel(FA_PAIRED_ARGS) {
+  bwd_paired_body<D, true>(Q, K, V, L2, ND, dO, dQ, dK, dV, N, scale, neg, ns, kvpart, qpart);
+}
+#undef FA_PAIRED_ARGS
 
 // Adds the ns partial [64][D] fp32 tiles that bwd_causal_paired_kernel or bwd_kernel wrote for
 // each 64-row tile when it spread every workgroup's steps over ns workgroups, scales dK and dQ,
@@ -1764,6 +1784,7 @@ enum BwdKernel { kBwdPlain, kBwdPaired };
 struct BwdPlan {
   BwdKernel kernel;
   int ns;
+  bool lean;  // paired grids of two to three workgroups per CU: the lean kernel, one round
 };
 
 BwdPlan bwd_plan(const Shape& s, size_t ws_bytes, bool ws_aligned16) {
@@ -1772,7 +1793,9 @@ BwdPlan bwd_plan(const Shape& s, size_t ws_bytes, bool ws_aligned16) {
   const size_t split_bytes = (size_t)(s.Nq / 64) * s.BH * ns * 3 * 64 * s.d * sizeof(float);
   if (ns > 1 && (ws_bytes < (size_t)rows * 2 * sizeof(float) + split_bytes || !ws_aligned16))
     ns = 1;  // the partial tiles are written and read 16 bytes at a time
-  return {bwd_uses_paired(s) ? kBwdPaired : kBwdPlain, ns};
+  const bool paired = bwd_uses_paired(s);
+  const long long wgs = (long long)(s.Nq / 64) * s.BH * ns;
+  return {paired ? kBwdPaired : kBwdPlain, ns, paired && wgs > 2 * kNumCUs};
 }
 
 template <int D, bool CAUSAL>
@@ -1791,10 +1814,16 @@ hipError_t bwd_t(const Shape& s, const void* Q, const void* K, const void* V, co
   bool launched = false;
   if constexpr (CAUSAL && D >= 32 && D <= 64) {
     if (pl.kernel == kBwdPaired) {
-      hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(tiles * ns)), dim3(256),
-                         0, stream, (const bf16*)Q, (const bf16*)K, (const bf16*)V, L2, ND,
-                         (const bf16*)dO, (bf16*)dQ, (bf16*)dK, (bf16*)dV, s.Nq, s.scale,
-                         s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
+      if (pl.lean)
+        hipLaunchKernelGGL((bwd_causal_paired_lean_kernel<D>), dim3((unsigned)(tiles * ns)),
+                           dim3(256), 0, stream, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, L2, ND, (const bf16*)dO, (bf16*)dQ, (bf16*)dK,
+                           (bf16*)dV, s.Nq, s.scale, s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
+      else
+        hipLaunchKernelGGL((bwd_causal_paired_kernel<D>), dim3((unsigned)(tiles * ns)),
+                           dim3(256), 0, stream, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, L2, ND, (const bf16*)dO, (bf16*)dQ, (bf16*)dK,
+                           (bf16*)dV, s.Nq, s.scale, s.scale < 0.f ? 1 : 0, ns, kvpart, qpart);
       launched = true;
     }
   }
@@ -1833,6 +1862,8 @@ const char* const kBwdPlainNames[2][4] = {
      "bwd_kernel<128, false>"},
     {"bwd_kernel<16, true>", "bwd_kernel<32, true>", "bwd_kernel<64, true>",
      "bwd_kernel<128, true>"}};
+const char* const kBwdPairedLeanNames[4] = {"", "bwd_causal_paired_lean_kernel<32>",
+                                            "bwd_causal_paired_lean_kernel<64>", ""};
 const char* const kBwdPairedNames[4] = {"", "bwd_causal_paired_kernel<32>",
                                         "bwd_causal_paired_kernel<64>", ""};
 
@@ -1936,7 +1967,7 @@ const char* fwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes) {
 const char* bwd_kernel_name_bf16(const Shape& s, size_t workspace_bytes) {
   const BwdPlan pl = bwd_plan(s, workspace_bytes, true);
   const int di = d_index(s.d);
-  if (pl.kernel == kBwdPaired) return kBwdPairedNames[di];
+  if (pl.kernel == kBwdPaired) return pl.lean ? kBwdPairedLeanNames[di] : kBwdPairedNames[di];
   return kBwdPlainNames[s.causal ? 1 : 0][di];
 }
 
