@@ -359,7 +359,7 @@ def test_split_forward_growing_scores(gpu, case):
 
 
 # Grids between one and two tile pairs per CU: the forward takes the four-wave paired kernel
-# (two per CU), the backward the lean paired kernel (three per CU, one round).
+# (two per CU), the backward the lean paired kernel (three per CU, all at once).
 MID = [(4, 9, 1024, 32), (2, 17, 1024, 64)]
 
 

@@ -1357,8 +1357,8 @@ __device__ __forceinline__ void stream3(int first, int last, bf16* __restrict__ 
 //
 // LEAN reads each step's transposed operands where the products use them instead of up front
 // (kv_step and q_step with EARLY = false), which fits three workgroups per CU (168 VGPRs):
-// bwd_causal_paired_lean_kernel runs grids of two to three workgroups per CU in one round,
-// where two per CU would need a second, half-empty round.
+// bwd_causal_paired_lean_kernel runs grids of two to three workgroups per CU all at once,
+// where two per CU would leave a second, half-empty wave of workgroups.
 template <int D, bool LEAN>
 __device__ __forceinline__ void bwd_paired_body(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -1784,7 +1784,7 @@ enum BwdKernel { kBwdPlain, kBwdPaired };
 struct BwdPlan {
   BwdKernel kernel;
   int ns;
-  bool lean;  // paired grids of two to three workgroups per CU: the lean kernel, one round
+  bool lean;  // paired grids of two to three workgroups per CU: the lean kernel, all resident
 };
 
 BwdPlan bwd_plan(const Shape& s, size_t ws_bytes, bool ws_aligned16) {
