@@ -314,8 +314,8 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
 
   auto fetch = [&](int n, bf16 (*dst)[KT]) {
     const int k0 = kt_of(n) * BK;
-    KTile::template load<2>(Kr, k0, dst[0], wp, lane);
-    KTile::template load<2>(Vr, k0, dst[1], wp, lane);
+    KTile::template load_in_range<2>(Kr, k0, dst[0], wp, lane);
+    KTile::template load_in_range<2>(Vr, k0, dst[1], wp, lane);
   };
   auto finish_B = [&]() {  // pair 1, after B's last key tile: B is complete
     if (ns > 1) {
@@ -516,8 +516,8 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
   };
   auto fetch = [&](int n, int b) {
     const int k0 = (n < nA ? n : n - nA) * BK;
-    KTile::template load<2>(Kr, k0, kv[pr][b][0], wp, lane);
-    KTile::template load<2>(Vr, k0, kv[pr][b][1], wp, lane);
+    KTile::template load_in_range<2>(Kr, k0, kv[pr][b][0], wp, lane);
+    KTile::template load_in_range<2>(Vr, k0, kv[pr][b][1], wp, lane);
   };
 
   if (st < en) fetch(st, 0);
@@ -761,16 +761,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16* __restrict__ 
 
 // Direct loads of the dK/dV stream for moving tile m0.. (Q and dO rows, L2 and ND) into
 // `buf`, by NW >= 2 waves (index w). Rows past Nq read as zeros: their Q, dO and ND are 0, so
-// their P = exp2(0) = 1 meets dO = 0 and dP - D = 0 and adds nothing to dV or dK.
-template <int D, int NW>
+// their P = exp2(0) = 1 meets dO = 0 and dP - D = 0 and adds nothing to dV or dK. IN_RANGE
+// (the tile lies inside the head) takes the tile's offset as a wave-uniform operand.
+template <int D, int NW, bool IN_RANGE = false>
 __device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc_t NDr, int m0,
                                          bf16* buf, int w, int lane) {
   static_assert(NW >= 2, "L2 and ND are fetched by waves 0 and 1");
   using B = Bwd<D>;
-  B::MTile::template load<NW>(Qr, m0, buf, w, lane);
-  B::MTile::template load<NW>(dOr, m0, buf + B::T, w, lane);
-  if (w < 2 && lane < 32)
-    dma4(w == 0 ? L2r : NDr, (uint32_t)(m0 + lane) * 4, buf + 2 * B::T + 64 * w);
+  if constexpr (IN_RANGE) {
+    B::MTile::template load_in_range<NW>(Qr, m0, buf, w, lane);
+    B::MTile::template load_in_range<NW>(dOr, m0, buf + B::T, w, lane);
+    if (w < 2 && lane < 32)
+      dma4_at(w == 0 ? L2r : NDr, (uint32_t)lane * 4, (uint32_t)m0 * 4, buf + 2 * B::T + 64 * w);
+  } else {
+    B::MTile::template load<NW>(Qr, m0, buf, w, lane);
+    B::MTile::template load<NW>(dOr, m0, buf + B::T, w, lane);
+    if (w < 2 && lane < 32)
+      dma4(w == 0 ? L2r : NDr, (uint32_t)(m0 + lane) * 4, buf + 2 * B::T + 64 * w);
+  }
 }
 
 // Transposed LDS operands of one dK/dV step (dO^T and Q^T, the A operands of dV^T and dK^T).
@@ -1425,7 +1433,9 @@ __device__ __forceinline__ void bwd_paired_body(
     constexpr int kKeep = B::MTile::NKIB + 1;
     stream3<kKeep>(
         n_lo, n_hi, smem[pr][0], smem[pr][1], smem[pr][2],
-        [&](int n, bf16* dst) { kv_fetch<D, 2>(Qr, dOr, L2r, NDr, 32 * mt_of(n), dst, wp, lane); },
+        [&](int n, bf16* dst) {
+          kv_fetch<D, 2, true>(Qr, dOr, L2r, NDr, 32 * mt_of(n), dst, wp, lane);
+        },
         [&](int n, bf16* buf) {
           const int m0 = 32 * mt_of(n);
           const int kw0 = 64 * kt + 32 * wp;
@@ -1525,8 +1535,8 @@ __device__ __forceinline__ void bwd_paired_body(
     stream3<kKeep>(
         n_lo, n_hi, smem[pr][0], smem[pr][1], smem[pr][2],
         [&](int n, bf16* dst) {
-          B::MTile::template load<2>(Kr, 32 * kt_of(n), dst, wp, lane);
-          B::MTile::template load<2>(Vr, 32 * kt_of(n), dst + B::T, wp, lane);
+          B::MTile::template load_in_range<2>(Kr, 32 * kt_of(n), dst, wp, lane);
+          B::MTile::template load_in_range<2>(Vr, 32 * kt_of(n), dst + B::T, wp, lane);
         },
         [&](int n, bf16* buf) {
           const int n0 = 32 * kt_of(n);

@@ -227,6 +227,19 @@ __device__ __forceinline__ void dma16(rsrc_t src, uint32_t byte_off, void* dst) 
 __device__ __forceinline__ void dma4(rsrc_t src, uint32_t byte_off, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 4, byte_off, 0, 0, 0);
 }
+// dma16 and dma4 with the offset split into a per-lane part and a wave-uniform part, which goes
+// in the instruction's scalar offset operand. For loads that lie inside the buffer: the zero
+// fill of bytes past its end, which dma16 and dma4 give, is not relied on here.
+__device__ __forceinline__ void dma16_at(rsrc_t src, uint32_t lane_off, uint32_t uniform_off,
+                                         void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 16, lane_off, (int)uniform_off,
+                                           0, 0);
+}
+__device__ __forceinline__ void dma4_at(rsrc_t src, uint32_t lane_off, uint32_t uniform_off,
+                                        void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)dst, 4, lane_off, (int)uniform_off,
+                                           0, 0);
+}
 
 // Row-major R x C bf16 LDS tile with 16-byte chunks XOR-swizzled by row (swz in fa_common.h).
 template <int R, int C>
@@ -248,6 +261,24 @@ struct Tile {
         const int row = p / NCH, cp = p % NCH;
         const int gc = cp ^ swz_key<NCH>(row);
         dma16(src, (uint32_t)(((row0 + row) * C + gc * 8) * 2), t + blk * 512);
+      }
+    }
+  }
+  // load() for a tile that lies wholly inside the head (row0 + R <= its rows): the row offset
+  // is wave-uniform (dma16_at), so each lane's offset is the same for every tile and no vector
+  // instruction forms it again per tile.
+  template <int NW>
+  __device__ __forceinline__ static void load_in_range(rsrc_t src, int row0, bf16* t, int w,
+                                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < (NKIB + NW - 1) / NW; ++i) {
+      const int blk = w + i * NW;
+      if (NKIB % NW == 0 || blk < NKIB) {
+        const int p = blk * 64 + lane;
+        const int row = p / NCH, cp = p % NCH;
+        const int gc = cp ^ swz_key<NCH>(row);
+        dma16_at(src, (uint32_t)((row * C + gc * 8) * 2), (uint32_t)row0 * (C * 2),
+                 t + blk * 512);
       }
     }
   }
