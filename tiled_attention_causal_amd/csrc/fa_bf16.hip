@@ -782,12 +782,12 @@ __device__ __forceinline__ void kv_fetch(rsrc_t Qr, rsrc_t dOr, rsrc_t L2r, rsrc
 }
 
 // Transposed LDS operands of one dK/dV step (dO^T and Q^T, the A operands of dV^T and dK^T).
-// The paired kernel requests them at the start of the step, before the next tile's direct
-// loads are issued: the compiler cannot tell that those loads do not alias a transposed read,
-// and would otherwise wait for them to land first. That costs 8 * DB registers for the whole
-// step, which bwd_kernel cannot afford without dropping from three waves per SIMD to two, so
-// there kv_step reads them where they are used (EARLY = false) and takes the wait, which the
-// first half of the step overlaps. Plain LDS reads do not have this problem.
+// The paired kernel requests them at the start of the step, right behind the reads its first
+// products wait for (kv_step with EARLY = true), so that they are in flight while those
+// products and the exponentials run. That costs 8 * DB registers for the whole step, which
+// bwd_kernel cannot afford without dropping from three waves per SIMD to two, so there
+// kv_step reads them where they are used (EARLY = false) and takes the wait, which the first
+// half of the step overlaps.
 template <int D>
 struct KvOps {
   static constexpr int DB = (D + 31) / 32;
@@ -813,7 +813,7 @@ struct KvOps {
 // With DSOUT, dS (bf16, as the dK product takes it) is also written to dsT, a 32 x 32 LDS
 // tile of this wave (Tile<32, 32> layout, row = key, column = query), for a dQ product.
 template <int D, bool EARLY, bool DSOUT = false>
-__device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
+__device__ __forceinline__ void kv_step(const bf16* buf, KvOps<D>& op,
                                         const bf16x8 (&kf)[D / 16],
                                         const bf16x8 (&vf)[D / 16],
                                         f32x16 (&dvt)[(D + 31) / 32],
@@ -822,12 +822,8 @@ __device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
                                         bf16* dsT = nullptr) {
   using B = Bwd<D>;
   constexpr int DS = D / 16, DB = (D + 31) / 32;
-  bf16x8 qa[DS], da[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    qa[s] = B::MTile::frag(buf, l32, 2 * s + g);
-    da[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
-  }
+  // LDS reads in the order they are needed: dP's starting value, the score products' row
+  // fragments, then (EARLY) the transposed operands of the last products.
   const float* sL2 = reinterpret_cast<const float*>(buf + 2 * B::T);
   f32x16 sp = zero16(), dp;
 #pragma unroll
@@ -836,9 +832,18 @@ __device__ __forceinline__ void kv_step(const bf16* buf, const KvOps<D>& op,
 #pragma unroll
     for (int i = 0; i < 4; ++i) dp[4 * j + i] = n4[i];
   }
+  bf16x8 qa[DS], da[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    qa[s] = B::MTile::frag(buf, l32, 2 * s + g);
+    da[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
+  }
   // With registers to spare (EARLY), all of these reads are issued before the first MFMA,
   // so the score MFMAs wait for one LDS round trip rather than one per operand pair.
-  if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
+  if constexpr (EARLY) {
+    op.read(buf, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     sp = mfma32(qa[s], kf[s], sp);
@@ -903,7 +908,7 @@ struct QOps {
 // 8(r/4) + 4g + r%4), P = exp2(S c - L2), dS = P (dP - D), dQ^T += K^T dS^T. When `masked`,
 // keys with offset above hi get P = dS = 0.
 template <int D, bool EARLY>
-__device__ __forceinline__ void q_step(const bf16* buf, const QOps<D>& op,
+__device__ __forceinline__ void q_step(const bf16* buf, QOps<D>& op,
                                        const bf16x8 (&qf)[D / 16],
                                        const bf16x8 (&dof)[D / 16],
                                        f32x16 (&dqt)[(D + 31) / 32], float c, float l2,
@@ -917,7 +922,10 @@ __device__ __forceinline__ void q_step(const bf16* buf, const QOps<D>& op,
     k[s] = B::MTile::frag(buf, l32, 2 * s + g);
     v[s] = B::MTile::frag(buf + B::T, l32, 2 * s + g);
   }
-  if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);  // as in kv_step
+  if constexpr (EARLY) {  // as in kv_step: the transposed operands after the row fragments
+    op.read(buf, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   f32x16 st[1] = {zero16()};
   f32x16 dpt = splat16(nd);  // dP starts at -D of this lane's query
 #pragma unroll
@@ -1441,7 +1449,6 @@ __device__ __forceinline__ void bwd_paired_body(
           const int kw0 = 64 * kt + 32 * wp;
           if (m0 + 31 >= kw0) {
             KvOps<D> op;
-            if constexpr (!LEAN) op.read(buf, lane);
             kv_step<D, !LEAN>(buf, op, kf, vf, dvt, dkt, c, m0 < kw0 + 31, krow - m0 - 4 * g,
                               lane, l32, g);
           }
@@ -1543,7 +1550,6 @@ __device__ __forceinline__ void bwd_paired_body(
           const int qw0 = 64 * qt + 32 * wp;
           if (n0 <= qw0 + 31) {
             QOps<D> op;
-            if constexpr (!LEAN) op.read(buf, lane);
             q_step<D, !LEAN>(buf, op, row.qf, row.dof, dqt, c, row.l2, row.nd, n0 + 31 > qw0,
                              qrow - n0 - 4 * g, lane, l32, g);
           }
