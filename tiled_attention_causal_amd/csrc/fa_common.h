@@ -173,10 +173,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   permlane32_swap(a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
+// The IEEE 754-2019 maximum (one v_maximum3_f32): fmaxf would first canonicalise both
+// values, which come out of inline asm. The two differ only for NaN operands and for the sign
+// of a zero maximum, and neither changes a softmax computed from the result.
 __device__ __forceinline__ float halves_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   permlane32_swap(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // Workgroups are dispatched round-robin over the eight XCDs (workgroup b runs on XCD b % 8).
