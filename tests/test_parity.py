@@ -115,6 +115,8 @@ SMALL = [
     (1, 1, 150, 90, 64, "f32", False),
     (2, 1, 70, 70, 128, "f32", True),
     (1, 1, 33, 65, 16, "f32", False),
+    (1, 2, 150, 230, 16, "bf16", False),
+    (1, 1, 200, 130, 32, "f32", False),
     # fp32 over several 128-row workgroups and 32-row steps, ragged ends included
     (1, 2, 600, 600, 64, "f32", True),
     (1, 1, 384, 520, 128, "f32", False),
