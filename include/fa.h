@@ -278,7 +278,7 @@ FA_API fa_status fa_backward_noalloc(fa_dtype dtype, int64_t B, int64_t H, int64
  * fa_forward_kernel_name, fa_backward_kernel_name -- the name, as a profiler lists it, of the
  * attention kernel that fa_forward_with_workspace (fa_forward: workspace_bytes = 0) or
  * fa_backward / fa_backward_main with `workspace_bytes` of workspace launch for these
- * arguments, for example "fwd_causal_split_kernel<64>" (the library's choice of kernel
+ * arguments, for example "fwd_causal_wide_kernel<64>" (the library's choice of kernel
  * depends on the grid's size and shape, and on the workspace). The launchers take the same
  * decision from the same code. Static storage, never NULL; "" for arguments the calls would
  * reject.

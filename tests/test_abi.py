@@ -314,7 +314,7 @@ def test_kernel_names_follow_dispatch(lib):
         return (lib.fa_forward_kernel_name(dtype, B, H, Nq, Nk, d, causal, fws).decode(),
                 lib.fa_backward_kernel_name(dtype, B, H, Nq, Nk, d, causal, bws).decode())
     # 8 heads of 4096 at d = 64, causal: 256 tile pairs fill the CUs once
-    assert names(1, 8, 1, 4096, 4096, 64, 1) == ("fwd_causal_split_kernel<64>",
+    assert names(1, 8, 1, 4096, 4096, 64, 1) == ("fwd_causal_wide_kernel<64>",
                                                  "bwd_causal_paired_kernel<64>")
     # 768 backward workgroups: the lean kernel runs them three per CU, all at once
     assert names(1, 4, 12, 1024, 1024, 64, 1) == ("fwd_causal_paired_kernel<64>",

@@ -33,7 +33,7 @@ def test_plain_attention_matches_oracle(n, d):
 
 def test_kernel_names_follow_dispatch():
     assert bench.kernel_names(WORKLOADS["b8_n4096_d64"]) == (
-        "fwd_causal_split_kernel<64>", "bwd_causal_paired_kernel<64>")
+        "fwd_causal_wide_kernel<64>", "bwd_causal_paired_kernel<64>")
     assert bench.kernel_names(WORKLOADS["xl_noncausal"]) == (
         "fwd_kernel<64, false>", "bwd_kernel<64, false>")
     assert bench.kernel_names(WORKLOADS["long_n16384_d128"]) == (

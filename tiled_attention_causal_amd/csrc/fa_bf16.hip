@@ -441,7 +441,8 @@ __global__ __launch_bounds__(256) void fwd_causal_paired_kernel(
   }
 }
 
-// Causal forward for Nq = Nk = N, N % 128 == 0, d <= 64, on eight waves (two per SIMD).
+// Causal forward for Nq = Nk = N, N % 128 == 0, d = 16 or 32 (d = 64 takes
+// fwd_causal_wide_kernel below), on eight waves (two per SIMD).
 //
 // As in fwd_causal_paired_kernel, workgroup i takes the 64-row query tiles A = T-1-i and
 // B = i (T = N/64), which need T + 1 key steps together: A over key tiles 0 .. T-i-1, then
@@ -644,9 +645,224 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
 }
 
 
-// Merges the ns partial records fwd_causal_split_kernel wrote for each 64-row tile (when it
-// spreads a tile pair over ns <= kMaxWays workgroups) with the online-softmax rescale, and
-// stores O and L. One workgroup per tile with 128 threads per 32-column block: thread t takes
+// fwd_causal_split_kernel with one wave per run instead of a wave pair: eight waves, two per
+// SIMD, each holding the query tile's 64 rows as two 32-row blocks, so the tile pair's T + 1
+// key steps are cut into 8 ns runs. A wave reads each K/V fragment once for both blocks (half
+// the LDS reads of a pair, which reads every fragment in both of its waves) and streams its
+// own tiles through one LDS slot: it copies the tile's fragments into registers, then loads
+// the next tile into the same slot while the products and exponentials run. No other wave
+// touches the slot, so the waves need no barrier between steps. At the end every wave parks
+// its last partial (an empty run parks m = -inf, l = O = 0) and all eight merge, each one
+// 32-column half of one 32-row block: waves 0-3 tile A, waves 4-7 tile B. Used for d = 64,
+// where it runs about 2% faster than the wave-pair kernel with bitwise-identical results.
+template <int D>
+__global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ Lout, int N, float scale, int neg, int ns,
+    float* __restrict__ part) {
+  constexpr int NW = 8, BK = 64;
+  constexpr int DS = D / 16, DB = (D + 31) / 32;
+  using KTile = Tile<BK, D>;
+  constexpr int KT = KTile::ELEMS;
+  constexpr int XS = 16 * DB + 2;  // parked partial: O registers, m, l (component-major)
+  // K/V slots, padded so that the eight parked partials fit in them.
+  constexpr int KTS = KT > 128 * XS ? KT : 128 * XS;
+  static_assert(KTS * 2 % 256 == 0, "K/V slots must keep the bank mapping");
+  __shared__ __attribute__((aligned(1024))) bf16 kv[NW][2][KTS];  // [wave][K | V]
+  __shared__ __attribute__((aligned(16))) float park_cross[XS * 128];
+  static_assert(NW * XS * 128 * sizeof(float) <= sizeof(kv), "parked partials must fit in kv");
+
+  const int T = N / 64, half = T / 2;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int sw = lid % ns, pid = lid / ns;  // this workgroup's share of tile pair pid
+  const int bh = pid / half, i = pid % half;
+  const int tA = T - 1 - i, tB = i, nA = T - i, S = T + 1;
+  const rsrc_t Qr = make_rsrc(Q + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Kr = make_rsrc(K + (size_t)bh * N * D, (uint32_t)N * D * 2);
+  const rsrc_t Vr = make_rsrc(V + (size_t)bh * N * D, (uint32_t)N * D * 2);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
+  const int NR = NW * ns;  // runs per tile pair, over all ns workgroups
+  const int st = (sw * NW + w) * S / NR, en = (sw * NW + w + 1) * S / NR;  // this wave's run
+  const float cs = fabsf(scale);
+  const float c = exp2_coef(scale);
+
+  bf16x8 qf[2][DS];  // the current query tile's two row blocks
+  auto load_q = [&](int qt) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      load_frags<D>(qf[rb], Qr, 64 * qt + 32 * rb + l32, g);
+      if (neg)
+#pragma unroll
+        for (int q = 0; q < DS; ++q) qf[rb][q] = negate(qf[rb][q]);
+    }
+  };
+  load_q(st < nA ? tA : tB);
+
+  f32x16 o[2][DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = zero16();
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+  // Record layout as in fwd_causal_split_kernel, row block rb in the place of wave wp.
+  auto park = [&](float* rec) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float* x = rec + rb * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[rb][db][r];
+      x[16 * DB * 128] = m[rb];
+      x[(16 * DB + 1) * 128] = l[rb];
+    }
+  };
+  const bf16* sK = kv[w][0];
+  const bf16* sV = kv[w][1];
+  auto fetch = [&](int n) {
+    const int k0 = (n < nA ? n : n - nA) * BK;
+    KTile::template load_in_range<1>(Kr, k0, kv[w][0], 0, lane);
+    KTile::template load_in_range<1>(Vr, k0, kv[w][1], 0, lane);
+  };
+
+  if (st < en) fetch(st);
+  wait_vmem();
+  for (int n = st; n < en; ++n) {
+    bf16x8 vfr[4][DB], kfr[2][DS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < DS; ++q) kfr[kb][q] = KTile::frag(sK, 32 * kb + l32, 2 * q + g);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vfr[u][db] = KTile::tfrag(sV, 32 * db, 16 * u, lane);
+    const bool isA = n < nA;
+    const int qt = isA ? tA : tB, kt = isA ? n : n - nA;
+    const bool first = n == st || n == nA;
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[rb][kb] = zero16();
+#pragma unroll
+        for (int q = 0; q < DS; ++q) sacc[rb][kb] = mfma32(kfr[kb][q], qf[rb][q], sacc[rb][kb]);
+      }
+    // Every fragment of the tile is in registers once the LDS reads have returned; the next
+    // tile then goes into the same slot while this one's products run.
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 1 < en) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      fetch(n + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (kt == qt) mask_scores<2>(sacc[rb], 0, 32 * rb + l32 - 4 * g);  // the diagonal tile
+      softmax_tile(sacc[rb], m[rb], l[rb], o[rb], c, first);
+      bf16x8 pf[4];
+      p_operands(sacc[rb], pf, l[rb]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] = mfma32(vfr[u][db], pf[u], o[rb][db]);
+    }
+    if (n + 1 == nA && n + 1 < en) {  // the run continues into B: park A's partial
+      park(park_cross);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] = zero16();
+        m[rb] = -INFINITY;
+        l[rb] = 0.f;
+      }
+      load_q(tB);
+    }
+    wait_vmem();
+  }
+
+  // Every wave parks its last partial (of A if its run ends within A, else of B; empty if
+  // its run is) in slot w once all waves are done with their K/V slots. Then each wave merges
+  // one 32-column half (db) of one 32-row block (rb) of tile A (waves 0-3) or B (4-7).
+  float* slots = reinterpret_cast<float*>(&kv[0][0][0]);
+  __syncthreads();
+  park(slots + w * XS * 128);
+  __syncthreads();
+  static_assert(DB == 2, "the merge gives each wave one of the two 32-column halves");
+  const bool mergeA = w < 4;
+  const int rb = (w >> 1) & 1, db = w & 1;
+  // Partials of the tile being merged: slot p holds tile A iff p's run ends within A; the
+  // crossing record holds A's part from the run that crosses into B, if one does. Every slot
+  // is read (weight 0 where it does not count), so the loads need not wait for each other.
+  bool inc[NW], cross = false;
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    const int sp = (sw * NW + p) * S / NR, ep = (sw * NW + p + 1) * S / NR;
+    inc[p] = sp < ep && (ep <= nA) == mergeA;
+    cross |= sp < nA && nA < ep;
+  }
+  cross = cross && mergeA;
+  const float* xc = park_cross + rb * 64 + lane;
+  float xm[NW], f[NW];
+  float mm = cross ? xc[16 * DB * 128] : -INFINITY;
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    xm[p] = slots[p * XS * 128 + 16 * DB * 128 + rb * 64 + lane];
+    if (inc[p]) mm = fmaxf(mm, xm[p]);
+  }
+  // An empty partial (m = -inf) weighs 0, also where every partial here is empty (ns > 1).
+  auto weight = [&](bool in, float m_) {
+    return in && m_ != -INFINITY ? fast_exp2((m_ - mm) * c) : 0.f;
+  };
+#pragma unroll
+  for (int p = 0; p < NW; ++p) f[p] = weight(inc[p], xm[p]);
+  float lsum = 0.f;
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    const float* x = slots + p * XS * 128 + rb * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += f[p] * x[(16 * db + r) * 128];
+    lsum += f[p] * x[(16 * DB + 1) * 128];
+  }
+  if (cross) {
+    const float fc = weight(true, xc[16 * DB * 128]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += fc * xc[(16 * db + r) * 128];
+    lsum += fc * xc[(16 * DB + 1) * 128];
+  }
+  if (ns > 1) {
+    // This workgroup's partial for the tile, as fwd_causal_split_kernel writes it.
+    float* x = part + ((size_t)pid * ns + sw) * 2 * (XS * 128) + (mergeA ? 0 : XS * 128) +
+               rb * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = acc[r];
+    if (db == 0) {
+      x[16 * DB * 128] = mm;
+      x[(16 * DB + 1) * 128] = lsum;
+    }
+    return;
+  }
+  const float lt = halves_sum(lsum);
+  const int row = 64 * (mergeA ? tA : tB) + 32 * rb + l32;
+  bf16* out = O + ((size_t)bh * N + row) * D + 32 * db;
+  const float inv = 1.f / lt;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (bf16)(acc[4 * j + k] * inv);
+    *reinterpret_cast<bf16x4*>(out + 8 * j + 4 * g) = v;
+  }
+  if (db == 0 && g == 0) Lout[(size_t)bh * N + row] = mm * cs + logf(lt);
+}
+
+// Merges the ns partial records fwd_causal_split_kernel or fwd_causal_wide_kernel wrote for
+// each 64-row tile (when it spreads a tile pair over ns <= kMaxWays workgroups) with the
+// online-softmax rescale, and stores O and L. One workgroup per tile with 128 threads per 32-column block: thread t takes
 // record lane t % 128 (lane = row, as in the split kernel) and column block t / 128, so every
 // load is coalesced and all of a thread's loads are independent. A record from a workgroup
 // with no part of the tile has m = -inf and l = O = 0, and so gets weight exp2(-inf) = 0.
@@ -1673,7 +1889,7 @@ int bwd_split_ways(const Shape& s) {
 }
 
 // Workgroups per tile pair of the causal small-grid forward kernels (the split kernel at
-// d <= 64; the paired kernel at d = 128). Small grids spread each pair's key steps over up
+// d = 16 and 32, the wide kernel at d = 64, the paired kernel at d = 128). Small grids spread each pair's key steps over up
 // to kMaxWays workgroups, doubling while the grid still fits the CUs (one such workgroup per
 // CU) and every wave pair keeps a run of at least kMinRun key steps; larger grids use one.
 constexpr int kMinRun = 4, kMaxWays = 8;
@@ -1683,7 +1899,8 @@ int fwd_split_ways(const Shape& s) {
   const long long pairs = (long long)(s.Nq / 128) * s.BH;
   if (pairs > kNumCUs) return 1;
   // Key steps of one wave pair's run per share: the split kernel cuts the pair's T + 1 steps
-  // into 4 runs, the paired kernel's longer run is T/2 + 1.
+  // into 4 runs, the paired kernel's longer run is T/2 + 1. (The wide kernel at d = 64 cuts
+  // them into 8 runs of half that length; the rule is kept the same for it.)
   const int steps = s.d <= 64 ? (s.Nq / 64 + 1) / 4 : s.Nq / 128 + 1;
   int ns = 1;
   while (ns < kMaxWays && pairs * ns * 2 <= kNumCUs && steps / (ns * 2) >= kMinRun) ns *= 2;
@@ -1716,7 +1933,8 @@ namespace {
 // launch whose partial results fwd_split_combine_kernel merges). Pairing pays off only when
 // one 128-query tile per workgroup leaves CUs idle or runs a single wave per SIMD anyway;
 // larger grids keep the plain kernel (shared K/V stream, two waves per SIMD). Up to one tile
-// pair per CU, d <= 64 takes the eight-wave split kernel and d = 128 the paired kernel; up
+// pair per CU, d <= 64 takes an eight-wave kernel (the wide kernel at d = 64, the split kernel
+// below that) and d = 128 the paired kernel; up
 // to two (d = 32, 64), the four-wave paired kernel (two fit a CU), whose balanced steps beat
 // the plain kernel's longest-tile tail.
 enum FwdKernel { kFwdPlain, kFwdPaired, kFwdSplit };
@@ -1747,7 +1965,11 @@ hipError_t fwd_t(const Shape& s, const void* Q, const void* K, const void* V, vo
     if (pl.kernel != kFwdPlain) {
       const unsigned grid = (unsigned)((long long)(s.Nq / 128) * s.BH * pl.ns);
       if (pl.kernel == kFwdSplit) {
-        if constexpr (D <= 64)
+        if constexpr (D == 64)
+          hipLaunchKernelGGL((fwd_causal_wide_kernel<D>), dim3(grid), dim3(512), 0, stream,
+                             (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L, s.Nq,
+                             s.scale, neg, pl.ns, ws);
+        else if constexpr (D <= 64)
           hipLaunchKernelGGL((fwd_causal_split_kernel<D>), dim3(grid), dim3(512), 0, stream,
                              (const bf16*)Q, (const bf16*)K, (const bf16*)V, (bf16*)O, L, s.Nq,
                              s.scale, neg, pl.ns, ws);
@@ -1872,7 +2094,7 @@ const char* const kFwdPairedNames[4] = {"", "fwd_causal_paired_kernel<32>",
                                         "fwd_causal_paired_kernel<128>"};
 const char* const kFwdSplitNames[4] = {"fwd_causal_split_kernel<16>",
                                        "fwd_causal_split_kernel<32>",
-                                       "fwd_causal_split_kernel<64>", ""};
+                                       "fwd_causal_wide_kernel<64>", ""};
 const char* const kBwdPlainNames[2][4] = {
     {"bwd_kernel<16, false>", "bwd_kernel<32, false>", "bwd_kernel<64, false>",
      "bwd_kernel<128, false>"},
