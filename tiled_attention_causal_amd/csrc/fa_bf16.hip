@@ -650,7 +650,7 @@ __global__ __launch_bounds__(512) void fwd_causal_split_kernel(
 // key steps are cut into 8 ns runs. A wave reads each K/V fragment once for both blocks (half
 // the LDS reads of a pair, which reads every fragment in both of its waves) and streams its
 // own tiles through one LDS slot: it copies the tile's fragments into registers, then loads
-// the next tile into the same slot while the products and exponentials run. No other wave
+// the next tile into the same slot while its second row block is computed. No other wave
 // touches the slot, so the waves need no barrier between steps. At the end every wave parks
 // its last partial (an empty run parks m = -inf, l = O = 0) and all eight merge, each one
 // 32-column half of one 32-row block: waves 0-3 tile A, waves 4-7 tile B. Used for d = 64,
@@ -751,12 +751,13 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
 #pragma unroll
         for (int q = 0; q < DS; ++q) sacc[rb][kb] = mfma32(kfr[kb][q], qf[rb][q], sacc[rb][kb]);
       }
-    // Every fragment of the tile is in registers once the LDS reads have returned; the next
-    // tile then goes into the same slot while this one's products run.
+    // Every fragment of the tile is in registers once the LDS reads have returned. The next
+    // tile goes into the same slot after row block 0's products are issued, while row block
+    // 1's softmax and products run (this placement measured faster than right after the
+    // score products, or later; so did waiting for the reads here rather than there).
     __builtin_amdgcn_sched_barrier(0);
     if (n + 1 < en) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      fetch(n + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -769,6 +770,11 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[rb][db] = mfma32(vfr[u][db], pf[u], o[rb][db]);
+      if (rb == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 1 < en) fetch(n + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (n + 1 == nA && n + 1 < en) {  // the run continues into B: park A's partial
       park(park_cross);
