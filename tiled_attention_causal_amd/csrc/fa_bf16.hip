@@ -684,7 +684,11 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 5, l32 = lane & 31;
   const int NR = NW * ns;  // runs per tile pair, over all ns workgroups
-  const int st = (sw * NW + w) * S / NR, en = (sw * NW + w + 1) * S / NR;  // this wave's run
+  // Run boundaries rounded up, so that the runs with an extra step come first. Run 0 starts
+  // at A's first key step and reaches B only when A is shorter than it, so the run that
+  // crosses into B (and waits there for B's query rows) is, on longer heads, a shorter run.
+  auto run_start = [&](int r) { return ((sw * NW + r) * S + NR - 1) / NR; };
+  const int st = run_start(w), en = run_start(w + 1);  // this wave's run
   const float cs = fabsf(scale);
   const float c = exp2_coef(scale);
 
@@ -807,7 +811,7 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
   bool inc[NW], cross = false;
 #pragma unroll
   for (int p = 0; p < NW; ++p) {
-    const int sp = (sw * NW + p) * S / NR, ep = (sw * NW + p + 1) * S / NR;
+    const int sp = run_start(p), ep = run_start(p + 1);
     inc[p] = sp < ep && (ep <= nA) == mergeA;
     cross |= sp < nA && nA < ep;
   }
