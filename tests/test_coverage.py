@@ -43,7 +43,7 @@ def parity_launches(lib):
     for n in tp.FULL + ["long_n16384_d128"]:
         w = WORKLOADS[n]
         cases.append((w.dtype, w.B, w.H, w.Nq, w.Nk, w.d, w.causal))
-    square_causal = tp.PAIRED + tp.SPLIT_WG + tp.GROWING + tp.MID + tp.ONE_SHARE
+    square_causal = tp.PAIRED + tp.WIDE_T + tp.SPLIT_WG + tp.GROWING + tp.MID + tp.ONE_SHARE
     cases += [("bf16", B, H, N, N, d, True) for (B, H, N, d) in square_causal]
     cases += [("bf16", B, H, N, N, d, c) for (B, H, N, d, c) in tp.SPLIT_BWD]
     cases += [("f32", B, H, N, N, d, c) for (B, H, N, d, c) in tp.SPLIT_F32]

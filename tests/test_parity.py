@@ -296,6 +296,27 @@ def test_paired_causal_kernels_match_oracle(gpu, case):
     compare(got, full_oracle(inp, True, scale), "bf16")
 
 
+# One head at d = 64 and T = N/64 from 6 to 50 key steps: the wide forward cuts each tile
+# pair's T + 1 steps into eight runs (rounded up), so across these T and the workgroups of
+# each, the crossing from tile A into B falls inside different runs or on a run boundary, and
+# runs are one to four steps long (one share per tile pair up to T = 26, two at T = 50).
+WIDE_T = [(1, 1, 384, 64), (1, 1, 768, 64), (1, 1, 1152, 64), (1, 1, 1664, 64),
+          (1, 1, 3200, 64)]
+
+
+@pytest.mark.parametrize("case", WIDE_T, ids=lambda c: "B{}H{}N{}d{}".format(*c))
+def test_wide_forward_runs_match_oracle(gpu, case):
+    from bench import kernel_names
+    B, H, N, d = case
+    note(f"wide forward runs case {case}")
+    fwd, _ = kernel_names(Workload("case", 0, B, H, N, N, d, "bf16", True))
+    assert fwd == "fwd_causal_wide_kernel<64>"
+    inp = make_inputs(B, H, N, N, d, "bf16", index=9600 + N)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = run_gpu(inp, True, scale, gpu)
+    compare(got, full_oracle(inp, True, scale), "bf16")
+
+
 # Causal square shapes few enough in tiles that the forward spreads each tile pair over
 # several workgroups and merges their partial softmax states in a second launch, and the
 # backward spreads each workgroup's steps likewise and adds the partial dQ, dK, dV up
