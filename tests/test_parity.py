@@ -530,6 +530,23 @@ def test_paired_causal_kernels_unusual_scale(gpu, scale):
             check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
 
 
+def test_wide_forward_negative_scale_across_crossings(gpu):
+    """A negative scale negates the query rows, also those the wide forward reloads where a
+    run crosses from tile A into B; at T = 18 that happens inside a run for several tile
+    pairs (at T = 6 above, every run ends on a tile boundary)."""
+    from bench import kernel_names
+    scale = -0.2
+    inp = make_inputs(1, 1, 1152, 1152, 64, "bf16", index=8550)
+    assert kernel_names(Workload("case", 0, 1, 1, 1152, 1152, 64, "bf16", True))[0] == \
+        "fwd_causal_wide_kernel<64>"
+    got = run_gpu(inp, True, scale, gpu)
+    ref = full_oracle(inp, True, scale)
+    a = [to_f64(inp[n][0, 0]) for n in ("q", "k", "v", "do")]
+    allow = o_rounding_allowance(*a, True, scale)
+    for n in ("O", "L", "dQ", "dK", "dV"):
+        check(n, got[n][0, 0], ref[n][0], "bf16", allowance=allow.get(n))
+
+
 def test_paired_and_plain_forward_agree(gpu):
     """The same inputs through the paired and plain kernels: the grid-size switch only
     changes the order of the key-tile sums, so O and L agree to fp32 rounding."""
