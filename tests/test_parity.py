@@ -300,8 +300,9 @@ def test_paired_causal_kernels_match_oracle(gpu, case):
 # pair's T + 1 steps into eight runs (rounded up), so across these T and the workgroups of
 # each, the crossing from tile A into B falls inside different runs or on a run boundary, and
 # runs are one to four steps long (one share per tile pair up to T = 26, two at T = 50).
+# At T = 8 and 24 (one share per pair) run 0 is the only run one step longer than the rest.
 WIDE_T = [(1, 1, 384, 64), (1, 1, 768, 64), (1, 1, 1152, 64), (1, 1, 1664, 64),
-          (1, 1, 3200, 64)]
+          (1, 1, 3200, 64), (1, 1, 512, 64), (3, 1, 1536, 64)]
 
 
 @pytest.mark.parametrize("case", WIDE_T, ids=lambda c: "B{}H{}N{}d{}".format(*c))
@@ -530,14 +531,17 @@ def test_paired_causal_kernels_unusual_scale(gpu, scale):
             check(n, got[n][0, h], ref[n][h], "bf16", allowance=allow.get(n))
 
 
-def test_wide_forward_negative_scale_across_crossings(gpu):
+@pytest.mark.parametrize("N", [1152, 1536])
+def test_wide_forward_negative_scale_across_crossings(gpu, N):
     """A negative scale negates the query rows, also those the wide forward reloads where a
     run crosses from tile A into B; at T = 18 that happens inside a run for several tile
-    pairs (at T = 6 above, every run ends on a tile boundary)."""
+    pairs (at T = 6 above, every run ends on a tile boundary); T = 24 is a one-share grid
+    where only run 0 is a step longer than the others."""
     from bench import kernel_names
+    note(f"wide forward negative scale N={N}")
     scale = -0.2
-    inp = make_inputs(1, 1, 1152, 1152, 64, "bf16", index=8550)
-    assert kernel_names(Workload("case", 0, 1, 1, 1152, 1152, 64, "bf16", True))[0] == \
+    inp = make_inputs(1, 1, N, N, 64, "bf16", index=8550 + N)
+    assert kernel_names(Workload("case", 0, 1, 1, N, N, 64, "bf16", True))[0] == \
         "fwd_causal_wide_kernel<64>"
     got = run_gpu(inp, True, scale, gpu)
     ref = full_oracle(inp, True, scale)
