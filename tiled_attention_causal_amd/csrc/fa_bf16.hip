@@ -711,17 +711,25 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
     for (int db = 0; db < DB; ++db) o[rb][db] = zero16();
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  // Record layout as in fwd_causal_split_kernel, row block rb in the place of wave wp.
+  // A parked record in LDS: O in 16-byte chunks (four consecutive accumulator registers of
+  // one lane; chunk j of row block rb at float ((rb * 4 DB + j) * 64 + lane) * 4, so a wave
+  // writes or reads one chunk index with 128-bit accesses over consecutive addresses), then m
+  // and l per (row block, lane). The partials written to global memory for ns > 1 keep
+  // fwd_causal_split_kernel's component-major layout, which the combine kernel reads.
+  constexpr int MOFF = 2 * 16 * DB * 64;
   auto park = [&](float* rec) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float* x = rec + rb * 64 + lane;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[(16 * db + r) * 128] = o[rb][db][r];
-      x[16 * DB * 128] = m[rb];
-      x[(16 * DB + 1) * 128] = l[rb];
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v = {o[rb][db][4 * j], o[rb][db][4 * j + 1], o[rb][db][4 * j + 2],
+                     o[rb][db][4 * j + 3]};
+          *reinterpret_cast<f32x4*>(rec + ((rb * 4 * DB + 4 * db + j) * 64 + lane) * 4) = v;
+        }
+      rec[MOFF + rb * 64 + lane] = m[rb];
+      rec[MOFF + 128 + rb * 64 + lane] = l[rb];
     }
   };
   const bf16* sK = kv[w][0];
@@ -806,8 +814,10 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
   const bool mergeA = w < 4;
   const int rb = (w >> 1) & 1, db = w & 1;
   // Partials of the tile being merged: slot p holds tile A iff p's run ends within A; the
-  // crossing record holds A's part from the run that crosses into B, if one does. Every slot
-  // is read (weight 0 where it does not count), so the loads need not wait for each other.
+  // crossing record holds A's part from the run that crosses into B, if one does. A wave
+  // loads only its tile's slots (the test is uniform over the wave), all of them into
+  // registers before it adds any, so the loads need not wait for each other; reading every
+  // slot with weight 0 for the others took twice the LDS reads and measured slower.
   bool inc[NW], cross = false;
 #pragma unroll
   for (int p = 0; p < NW; ++p) {
@@ -816,12 +826,15 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
     cross |= sp < nA && nA < ep;
   }
   cross = cross && mergeA;
-  const float* xc = park_cross + rb * 64 + lane;
+  const float* xc = park_cross + MOFF + rb * 64 + lane;
+  auto chunk = [&](const float* rec, int j) {
+    return *reinterpret_cast<const f32x4*>(rec + ((rb * 4 * DB + 4 * db + j) * 64 + lane) * 4);
+  };
   float xm[NW], f[NW];
-  float mm = cross ? xc[16 * DB * 128] : -INFINITY;
+  float mm = cross ? xc[0] : -INFINITY;
 #pragma unroll
   for (int p = 0; p < NW; ++p) {
-    xm[p] = slots[p * XS * 128 + 16 * DB * 128 + rb * 64 + lane];
+    xm[p] = slots[p * XS * 128 + MOFF + rb * 64 + lane];
     if (inc[p]) mm = fmaxf(mm, xm[p]);
   }
   // An empty partial (m = -inf) weighs 0, also where every partial here is empty (ns > 1).
@@ -832,18 +845,37 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
   for (int p = 0; p < NW; ++p) f[p] = weight(inc[p], xm[p]);
   float lsum = 0.f;
   f32x16 acc = zero16();
+  float xv[NW][17];
 #pragma unroll
   for (int p = 0; p < NW; ++p) {
-    const float* x = slots + p * XS * 128 + rb * 64 + lane;
+    const float* x = slots + p * XS * 128;
+    if (inc[p]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += f[p] * x[(16 * db + r) * 128];
-    lsum += f[p] * x[(16 * DB + 1) * 128];
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = chunk(x, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[p][4 * j + e] = v[e];
+      }
+      xv[p][16] = x[MOFF + 128 + rb * 64 + lane];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    if (inc[p]) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += f[p] * xv[p][r];
+      lsum += f[p] * xv[p][16];
+    }
   }
   if (cross) {
-    const float fc = weight(true, xc[16 * DB * 128]);
+    const float fc = weight(true, xc[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += fc * xc[(16 * db + r) * 128];
-    lsum += fc * xc[(16 * DB + 1) * 128];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = chunk(park_cross, j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] += fc * v[e];
+    }
+    lsum += fc * xc[128];
   }
   if (ns > 1) {
     // This workgroup's partial for the tile, as fwd_causal_split_kernel writes it.
