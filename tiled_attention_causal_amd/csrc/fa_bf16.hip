@@ -804,10 +804,11 @@ __global__ __launch_bounds__(512) void fwd_causal_wide_kernel(
   }
 
   // Every wave parks its last partial (of A if its run ends within A, else of B; empty if
-  // its run is) in slot w once all waves are done with their K/V slots. Then each wave merges
+  // its run is) in slot w, which is its own K/V slot: its reads of that slot have returned
+  // and no other wave touches it, so it parks as soon as its run ends. Then each wave merges
   // one 32-column half (db) of one 32-row block (rb) of tile A (waves 0-3) or B (4-7).
+  static_assert(XS * 128 * sizeof(float) == sizeof(kv[0]), "slot w is wave w's K/V slot");
   float* slots = reinterpret_cast<float*>(&kv[0][0][0]);
-  __syncthreads();
   park(slots + w * XS * 128);
   __syncthreads();
   static_assert(DB == 2, "the merge gives each wave one of the two 32-column halves");
